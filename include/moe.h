@@ -1,0 +1,190 @@
+/*
+ * moe.h - C ABI of libmoe: one GPU's share of an expert-parallel mixture-of-experts FFN layer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The layer (X-Stage paper, "X-Stage: An Overlooked Pipeline Stage for Communication-
+ * Computation Overlap in DiT Inference", Introduction, MoE-layer paragraph): a router selects
+ * k experts per token; Dispatch moves each token to its experts; every expert applies
+ * Linear-1 (hidden H -> 2I, gate and up halves), SwiGLU, and Linear-2 (I -> H); Combine sums
+ * each token's k expert outputs weighted by the router weights. The same page's expert-wave
+ * paragraph groups local experts into waves that order the tile work; Section 4 (the X-Stage
+ * design test and the MegaMoE discussion) moves ready Linear-1 tiles of later waves between
+ * the Linear-2 tiles of the current wave. Both orders compute identical bytes here.
+ *
+ * The four calls follow the stages: moe_plan (route + expert histogram + prefix scan +
+ * stable scatter + tile schedule), moe_dispatch (gather rows), moe_forward (persistent grouped
+ * GEMM: Linear-1 with fused SwiGLU, then Linear-2), moe_combine (router-weighted sum).
+ *
+ * Conventions for every call:
+ *   - bfloat16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
+ *   - Every pointer except `cfg`, `rt` and `bytes`/`layout` outputs is a DEVICE pointer owned
+ *     by the caller (for example a torch tensor's data_ptr()). The library never allocates,
+ *     frees or retains caller memory and keeps no global state between calls.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every device call
+ *     is asynchronous on that stream and performs no host synchronisation, except
+ *     moe_status_read, which synchronises the stream.
+ *   - Arguments are validated on the host before anything is launched; an invalid call
+ *     returns an error code and launches nothing. No call aborts or throws.
+ *   - moe_dispatch / moe_forward / moe_combine must be given the routing buffers and workspace
+ *     filled by a moe_plan with the same cfg, earlier on the same stream (or ordered after it).
+ *   - Calls on different streams must use different routing buffers and workspaces.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes. */
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, k > E, unknown schedule ...   */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but outside what the kernels implement (see limits)      */
+  MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_size() reports           */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed                    */
+  MOE_ERR_TIMEOUT = -5      /* a Linear-2 tile's bounded wait for its Linear-1 rows expired   */
+} moe_status_code;
+typedef int32_t moe_status;
+
+/* Tile orders of the persistent grouped GEMM (moe_config.schedule). */
+enum {
+  /* Expert-Wave order: Linear-1 tiles of wave 0, its Linear-2 tiles, then wave 1, ...
+     (X-Stage paper, Introduction, expert-wave paragraph: the original MegaMoE schedule). */
+  MOE_SCHED_EXPERT_WAVE = 0,
+  /* Cross-wave interleaving: Linear-1 tiles of wave w + lead_waves are spread evenly between
+     the Linear-2 tiles of wave w (X-Stage paper, Section 4.1 "reshape injection" and Section
+     4.2 on MegaMoE: ready Linear-1 work of later waves is moved between Linear-2 epilogues;
+     the lead is the dependency-derived threshold the paper calls D_knee). */
+  MOE_SCHED_INTERLEAVED = 1
+};
+
+/* Limits of this implementation (violations return MOE_ERR_UNSUPPORTED). */
+#define MOE_MAX_EXPERTS 1024 /* E                                        */
+#define MOE_MAX_TOPK 32      /* k                                        */
+#define MOE_DIM_MULTIPLE 64  /* H and I must be multiples of this        */
+
+typedef struct moe_config {
+  int32_t T;                /* tokens on this GPU (>= 1)                                        */
+  int32_t H;                /* hidden size (multiple of 64)                                      */
+  int32_t I;                /* expert intermediate size (multiple of 64); Linear-1 yields 2*I   */
+  int32_t E;                /* local experts (1..1024)                                           */
+  int32_t k;                /* experts per token (1..min(E, 32))                                 */
+  int32_t experts_per_wave; /* W >= 1; wave w holds experts [w*W, min(E, (w+1)*W))              */
+  int32_t schedule;         /* MOE_SCHED_*                                                       */
+  int32_t lead_waves;       /* interleaved order only: D >= 1 (0 means 1); ignored otherwise    */
+  int32_t num_workgroups;   /* persistent grid size; 0 = one per compute unit per occupancy slot */
+  int32_t tile_m;           /* rows per GEMM tile: 0 = chosen from T*k/E, else 32, 64, 128, 256 */
+  int32_t spin_limit;       /* bounded-wait iterations of a Linear-2 tile; 0 = default (~seconds)*/
+  int32_t flags;            /* must be 0 except MOE_FLAG_* bits below                            */
+  int32_t reserved[4];      /* must be 0                                                         */
+} moe_config;
+
+/* Test hook: make every Linear-2 tile wait for one Linear-1 completion that never comes, so the
+   bounded wait expires (after spin_limit iterations) and the kernel exits normally with
+   MOE_ERR_TIMEOUT recorded. Results are then undefined. Never set in production. */
+#define MOE_FLAG_FORCE_WAIT_TIMEOUT 0x1
+
+/* Routing buffers, written by moe_plan and read by the later calls (device pointers). */
+typedef struct moe_routing {
+  int32_t* topk_ids; /* [T, k]   expert of slot (t, j); j ascending = descending router logit  */
+  float* topk_w;     /* [T, k]   renormalised router weight of slot (t, j)                      */
+  int32_t* counts;   /* [E]      rows routed to each expert                                     */
+  int32_t* offsets;  /* [E + 1]  first dispatched row of each expert; offsets[E] = T*k          */
+  int32_t* perm;     /* [T*k]    perm[r] = flat slot t*k + j held by dispatched row r           */
+  int32_t* pos;      /* [T*k]    pos[t*k + j] = dispatched row of slot (t, j)                   */
+} moe_routing;
+
+/* Where moe_plan keeps its schedule inside the workspace (byte offsets from the workspace
+   base; all int32 arrays). Filled on the host by moe_workspace_layout. */
+typedef struct moe_ws_layout {
+  size_t total_bytes;   /* = moe_workspace_size                                     */
+  size_t header;        /* int32[16]: [0] error code, [1] task cursor, [2] task count,
+                           [3] m-block count, [4] tile_m, [5] L1 n-tiles per m-block,
+                           [6] L2 n-tiles per m-block                               */
+  size_t chunk_counts;  /* int32[E * chunks]: per-(expert, token chunk) counts, then bases */
+  size_t mblk_expert;   /* int32[max_mblk]                                        */
+  size_t mblk_row0;     /* int32[max_mblk]                                        */
+  size_t mblk_rows;     /* int32[max_mblk]                                        */
+  size_t mblk_ready;    /* int32[max_mblk]: Linear-1 tiles finished per m-block   */
+  size_t tasks;         /* int32[max_tasks]: bit 31 = Linear-2, bits 30..12 m-block, 11..0 n-tile */
+  int32_t chunks;       /* token chunks of the routing histogram                  */
+  int32_t max_mblk;
+  int32_t max_tasks;
+  int32_t tile_m;       /* rows per tile                                          */
+  int32_t tile_n1;      /* Linear-1 tile: output columns of A per tile (gate+up = 2x weight rows) */
+  int32_t tile_n2;      /* Linear-2 tile: output columns of Yd per tile            */
+  int32_t n1_tiles;     /* ceil(I / tile_n1)                                        */
+  int32_t n2_tiles;     /* ceil(H / tile_n2)                                        */
+} moe_ws_layout;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). Host only. */
+int32_t moe_abi_version(void);
+
+/* Static description of a status code. Never NULL. Host only. */
+const char* moe_strerror(moe_status status);
+
+/* Bytes of device workspace that moe_plan / moe_forward need for `cfg` (host only, no GPU
+   access). The workspace holds the routing histogram, the m-block table, the dependency
+   counters and the tile list. Errors: MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED as for
+   moe_plan. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Host-side description of the workspace layout for `cfg` (no GPU access). */
+moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* layout);
+
+/* Route and plan (X-Stage paper, Introduction, MoE-layer and expert-wave paragraphs).
+ *   logits [T, E] float32: router logits of this GPU's tokens over its E local experts.
+ * Writes every array of `rt` and the schedule in `ws`:
+ *   topk_ids/topk_w: per token the k largest logits in descending order (equal logits: lower
+ *     expert id first; -0 equals +0); weights = softmax restricted to the k kept logits
+ *     (the full softmax renormalised over them), float32. NaN logits are not supported.
+ *   counts/offsets/perm/pos: a stable counting sort of slots f = t*k + j by expert, so the
+ *     dispatched rows are expert-contiguous and, within an expert, in slot order.
+ *   ws: m-block table, zeroed dependency counters, and the Linear-1/Linear-2 tile list in
+ *     the order cfg->schedule asks for.
+ * Three kernel launches; no host synchronisation. */
+moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Dispatch: xd[r, :] = x[perm[r] / k, :] for r < T*k (bit copy).
+ *   x [T, H] bf16 in; xd [T*k, H] bf16 out (caller-allocated). */
+moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint16_t* x,
+                        uint16_t* xd, void* stream);
+
+/* Expert FFN over all dispatched rows in one persistent launch (plus a tiny counter reset).
+ *   xd  [T*k, H] bf16 dispatched rows (from moe_dispatch)
+ *   w1  [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up (out x in, like nn.Linear.weight)
+ *   w2  [E, H, I] bf16
+ *   act [T*k, I] bf16 out: A = bf16(silu(xd W_gate^T) * (xd W_up^T)), fp32 accumulation
+ *   yd  [T*k, H] bf16 out: Yd = bf16(A W2^T), fp32 accumulation
+ * Tiles run in the order moe_plan stored; every order gives the same bytes (each output
+ * element accumulates over k in the same fixed order). Experts with no rows read no weights.
+ * A Linear-2 tile that waits longer than the bounded spin records MOE_ERR_TIMEOUT in the
+ * workspace (read it with moe_status_read) and the kernel still exits. */
+moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t* w1,
+                       const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Combine: out[t, :] = bf16( sum_{j=0..k-1} topk_w[t, j] * yd[pos[t*k + j], :] ), fp32 sum in
+ * ascending j (fixed order, no atomics, deterministic).
+ *   yd [T*k, H] bf16 in; out [T, H] bf16 out. */
+moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd,
+                       uint16_t* out, void* stream);
+
+/* Synchronises `stream`, then returns the device-side error recorded in the workspace by the
+ * last moe_plan / moe_forward: MOE_OK, MOE_ERR_TIMEOUT (a bounded wait expired), or
+ * MOE_ERR_WORKSPACE (moe_forward found a tile that no moe_plan for this cfg could have written
+ * and skipped it); MOE_ERR_HIP if the stream reports a failure. */
+moe_status moe_status_read(const void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,54 @@
+"""One GPU's share of an expert-parallel MoE FFN layer on MI355X (gfx950).
+
+The compute lives in ``libmoe.so`` (hand-written HIP kernels behind the C ABI of
+``include/moe.h``). This package is the thin Python side: ``_lib`` marshals arguments to the
+four calls, and ``alloc_buffers`` / ``run_layer`` allocate device memory with torch and chain
+the calls on one stream. Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+from ._lib import (  # noqa: F401
+    MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
+    MOE_FLAG_FORCE_WAIT_TIMEOUT, MOE_OK, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, LIB_PATH,
+    MoeConfig, MoeError, abi_version, load, moe_combine, moe_dispatch, moe_forward, moe_plan,
+    moe_status_read, moe_workspace_layout, moe_workspace_size, strerror,
+)
+
+
+def alloc_routing(cfg: MoeConfig, device="cuda") -> dict:
+    """Device buffers for ``moe_routing`` (torch tensors)."""
+    import torch
+
+    R = cfg.T * cfg.k
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(
+        topk_ids=torch.empty((cfg.T, cfg.k), **i32),
+        topk_w=torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=device),
+        counts=torch.empty(cfg.E, **i32),
+        offsets=torch.empty(cfg.E + 1, **i32),
+        perm=torch.empty(R, **i32),
+        pos=torch.empty(R, **i32),
+    )
+
+
+def alloc_buffers(cfg: MoeConfig, device="cuda") -> dict:
+    """Routing buffers, workspace and the row buffers (xd, act, yd) plus the output."""
+    import torch
+
+    R = cfg.T * cfg.k
+    bf = dict(dtype=torch.bfloat16, device=device)
+    b = alloc_routing(cfg, device)
+    b["ws"] = torch.zeros(moe_workspace_size(cfg), dtype=torch.uint8, device=device)
+    b["xd"] = torch.empty((R, cfg.H), **bf)
+    b["act"] = torch.empty((R, cfg.I), **bf)
+    b["yd"] = torch.empty((R, cfg.H), **bf)
+    b["out"] = torch.empty((cfg.T, cfg.H), **bf)
+    return b
+
+
+def run_layer(cfg: MoeConfig, bufs: dict, x, logits, w1, w2, stream=None) -> None:
+    """plan -> dispatch -> forward -> combine on one stream (asynchronous)."""
+    moe_plan(cfg, logits, bufs, bufs["ws"], stream)
+    moe_dispatch(cfg, bufs, x, bufs["xd"], stream)
+    moe_forward(cfg, bufs["xd"], w1, w2, bufs["act"], bufs["yd"], bufs["ws"], stream)
+    moe_combine(cfg, bufs, bufs["yd"], bufs["out"], stream)

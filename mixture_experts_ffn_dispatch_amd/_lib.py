@@ -1,0 +1,193 @@
+"""ctypes binding of libmoe's C ABI (include/moe.h): argument marshalling only.
+
+Every step of the layer runs in the HIP library; this module turns torch tensors into device
+pointers and the current HIP stream into a handle, and raises ``MoeError`` on a non-zero
+status. There is no fallback: if ``libmoe.so`` is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+MOE_ERR_TIMEOUT = -5
+
+MOE_SCHED_EXPERT_WAVE = 0
+MOE_SCHED_INTERLEAVED = 1
+MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} ({status})")
+
+
+class CConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "H", "I", "E", "k", "experts_per_wave", "schedule", "lead_waves", "num_workgroups",
+        "tile_m", "spin_limit", "flags")] + [("reserved", ctypes.c_int32 * 4)]
+
+
+class CRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("topk_ids", "topk_w", "counts", "offsets", "perm", "pos")]
+
+
+class CLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
+        "tasks")] + [(n, ctypes.c_int32) for n in (
+            "chunks", "max_mblk", "max_tasks", "tile_m", "tile_n1", "tile_n2", "n1_tiles", "n2_tiles")]
+
+
+@dataclass
+class MoeConfig:
+    """Python mirror of ``moe_config``."""
+
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    experts_per_wave: int = 1
+    schedule: int = MOE_SCHED_EXPERT_WAVE
+    lead_waves: int = 0
+    num_workgroups: int = 0
+    tile_m: int = 0
+    spin_limit: int = 0
+    flags: int = 0
+    reserved: tuple = field(default=(0, 0, 0, 0))
+
+    def to_c(self) -> CConfig:
+        c = CConfig()
+        for n in ("T", "H", "I", "E", "k", "experts_per_wave", "schedule", "lead_waves", "num_workgroups",
+                  "tile_m", "spin_limit", "flags"):
+            setattr(c, n, int(getattr(self, n)))
+        for i, v in enumerate(self.reserved):
+            c.reserved[i] = int(v)
+        return c
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by ``mixture_experts_ffn_dispatch_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mixture_experts_ffn_dispatch_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    sig = {
+        "moe_abi_version": (ctypes.c_int32, []),
+        "moe_strerror": (ctypes.c_char_p, [ctypes.c_int32]),
+        "moe_workspace_size": (ctypes.c_int32, [P(CConfig), P(ctypes.c_size_t)]),
+        "moe_workspace_layout": (ctypes.c_int32, [P(CConfig), P(CLayout)]),
+        "moe_plan": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, ctypes.c_size_t, vp]),
+        "moe_dispatch": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
+        "moe_forward": (ctypes.c_int32, [P(CConfig), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "moe_combine": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
+        "moe_status_read": (ctypes.c_int32, [vp, ctypes.c_size_t, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load().moe_strerror(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load().moe_abi_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a torch tensor (or an int address / None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _cfg(cfg) -> CConfig:
+    return cfg if isinstance(cfg, CConfig) else cfg.to_c()
+
+
+def _routing(rt) -> CRouting:
+    r = CRouting()
+    for n in ("topk_ids", "topk_w", "counts", "offsets", "perm", "pos"):
+        setattr(r, n, _ptr(rt[n]) if rt.get(n) is not None else None)
+    return r
+
+
+def moe_workspace_size(cfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_workspace_size(ctypes.byref(_cfg(cfg)), ctypes.byref(n)), "moe_workspace_size")
+    return int(n.value)
+
+
+def moe_workspace_layout(cfg) -> dict:
+    L = CLayout()
+    _check(load().moe_workspace_layout(ctypes.byref(_cfg(cfg)), ctypes.byref(L)), "moe_workspace_layout")
+    return {n: int(getattr(L, n)) for n, _ in CLayout._fields_}
+
+
+def moe_plan(cfg, logits, rt: dict, ws, stream=None) -> None:
+    c = _cfg(cfg)
+    _check(load().moe_plan(ctypes.byref(c), _ptr(logits), ctypes.byref(_routing(rt)), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "moe_plan")
+
+
+def moe_dispatch(cfg, rt: dict, x, xd, stream=None) -> None:
+    _check(load().moe_dispatch(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(x), _ptr(xd),
+                               _stream(stream)), "moe_dispatch")
+
+
+def moe_forward(cfg, xd, w1, w2, act, yd, ws, stream=None) -> None:
+    _check(load().moe_forward(ctypes.byref(_cfg(cfg)), _ptr(xd), _ptr(w1), _ptr(w2), _ptr(act), _ptr(yd),
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_combine(cfg, rt: dict, yd, out, stream=None) -> None:
+    _check(load().moe_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(yd), _ptr(out),
+                              _stream(stream)), "moe_combine")
+
+
+def moe_status_read(ws, stream=None) -> int:
+    """Synchronises the stream and returns the device-side status code (0 = OK)."""
+    return int(load().moe_status_read(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))

@@ -1,0 +1,230 @@
+// C ABI of libmoe (declared in include/moe.h): argument validation, workspace layout and
+// kernel launches. Host code only; every call validates before it launches anything.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Rows per GEMM tile for a routing-average of T*k/E rows per expert.
+int auto_tile_m(const moe_config& c) {
+  const double avg = (double)c.T * c.k / c.E;
+  if (avg >= 768) return 256;
+  if (avg >= 192) return 128;
+  if (avg >= 48) return 64;
+  return 32;
+}
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (c->T < 1 || c->H < 1 || c->I < 1 || c->E < 1 || c->k < 1 || c->k > c->E) return MOE_ERR_INVALID_ARG;
+  if (c->experts_per_wave < 1) return MOE_ERR_INVALID_ARG;
+  if (c->schedule != MOE_SCHED_EXPERT_WAVE && c->schedule != MOE_SCHED_INTERLEAVED) return MOE_ERR_INVALID_ARG;
+  if (c->lead_waves < 0 || c->num_workgroups < 0 || c->spin_limit < 0) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~MOE_FLAG_FORCE_WAIT_TIMEOUT) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (c->reserved[i] != 0) return MOE_ERR_INVALID_ARG;
+  if (c->tile_m != 0 && c->tile_m != 32 && c->tile_m != 64 && c->tile_m != 128 && c->tile_m != 256)
+    return MOE_ERR_UNSUPPORTED;
+  if (c->E > MOE_MAX_EXPERTS || c->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+  if (c->H % MOE_DIM_MULTIPLE || c->I % MOE_DIM_MULTIPLE) return MOE_ERR_UNSUPPORTED;
+  // 32-bit buffer ranges: dispatched row buffers and one expert's weight slab
+  const unsigned long long R = (unsigned long long)c->T * (unsigned long long)c->k;
+  const unsigned long long lim = 0xFFFFFFFFull;
+  if (R > 0x7FFFFFFFull) return MOE_ERR_UNSUPPORTED;
+  if (R * (unsigned long long)c->H * 2ull > lim || R * (unsigned long long)c->I * 2ull > lim) return MOE_ERR_UNSUPPORTED;
+  if (4ull * (unsigned long long)c->I * (unsigned long long)c->H > lim) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
+  moe_status st = check_config(c);
+  if (st != MOE_OK) return st;
+  memset(L, 0, sizeof(*L));
+  const long long R = (long long)c->T * c->k;
+  const int BM = c->tile_m ? c->tile_m : auto_tile_m(*c);
+  const long long n1 = (c->I + kTileN1 - 1) / kTileN1;
+  const long long n2 = (c->H + kTileN2 - 1) / kTileN2;
+  const long long chunks = ((long long)c->T + kTokensPerChunk - 1) / kTokensPerChunk;
+  const long long active = R < c->E ? R : c->E;
+  const long long max_mblk = (R + active * (BM - 1)) / BM;
+  const long long max_tasks = max_mblk * (n1 + n2);
+  if (n1 > kTaskNtMask || n2 > kTaskNtMask) return MOE_ERR_UNSUPPORTED;
+  if (max_mblk >= (1ll << kTaskMblkBits) - 1) return MOE_ERR_UNSUPPORTED;
+  if (max_tasks > 0x7FFFFFFFll || chunks * c->E > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
+  L->chunks = (int32_t)chunks;
+  L->max_mblk = (int32_t)max_mblk;
+  L->max_tasks = (int32_t)max_tasks;
+  L->tile_m = BM;
+  L->tile_n1 = kTileN1;
+  L->tile_n2 = kTileN2;
+  L->n1_tiles = (int32_t)n1;
+  L->n2_tiles = (int32_t)n2;
+  size_t off = 0;
+  L->header = off;
+  off = align_up(off + HDR_SLOTS * 4, 256);
+  L->chunk_counts = off;
+  off = align_up(off + (size_t)chunks * c->E * 4, 256);
+  L->mblk_expert = off;
+  off = align_up(off + (size_t)max_mblk * 4, 256);
+  L->mblk_row0 = off;
+  off = align_up(off + (size_t)max_mblk * 4, 256);
+  L->mblk_rows = off;
+  off = align_up(off + (size_t)max_mblk * 4, 256);
+  L->mblk_ready = off;
+  off = align_up(off + (size_t)max_mblk * 4, 256);
+  L->tasks = off;
+  off = align_up(off + (size_t)max_tasks * 4, 256);
+  L->total_bytes = off;
+  return MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_strerror(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "success";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case MOE_ERR_WORKSPACE: return "workspace too small or not filled by moe_plan";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_TIMEOUT: return "Linear-2 tile timed out waiting for its Linear-1 rows";
+    default: return "unknown status";
+  }
+}
+
+moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* layout) {
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  return compute_layout(cfg, layout);
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st == MOE_OK) *bytes = L.total_bytes;
+  return st;
+}
+
+moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
+                    size_t ws_bytes, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if (!logits || !rt || !ws || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm ||
+      !rt->pos)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  PlanArgs a;
+  a.logits = logits;
+  a.topk_ids = rt->topk_ids;
+  a.topk_w = rt->topk_w;
+  a.counts = rt->counts;
+  a.offsets = rt->offsets;
+  a.perm = rt->perm;
+  a.pos = rt->pos;
+  a.hdr = at<int32_t>(ws, L.header);
+  a.chunk_counts = at<int32_t>(ws, L.chunk_counts);
+  a.mb_expert = at<int32_t>(ws, L.mblk_expert);
+  a.mb_row0 = at<int32_t>(ws, L.mblk_row0);
+  a.mb_rows = at<int32_t>(ws, L.mblk_rows);
+  a.mb_ready = at<int32_t>(ws, L.mblk_ready);
+  a.tasks = at<int32_t>(ws, L.tasks);
+  a.T = cfg->T;
+  a.E = cfg->E;
+  a.k = cfg->k;
+  a.chunks = L.chunks;
+  a.W = cfg->experts_per_wave > cfg->E ? cfg->E : cfg->experts_per_wave;
+  a.schedule = cfg->schedule;
+  a.lead = cfg->lead_waves > 0 ? cfg->lead_waves : 1;
+  a.tile_m = L.tile_m;
+  a.n1 = L.n1_tiles;
+  a.n2 = L.n2_tiles;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_scan_schedule(a, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_scatter(a, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint16_t* x, uint16_t* xd,
+                        void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!rt || !rt->perm || !x || !xd) return MOE_ERR_INVALID_ARG;
+  const int R = cfg->T * cfg->k;
+  if (launch_dispatch(rt->perm, x, xd, R, cfg->H, cfg->k, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t* w1, const uint16_t* w2,
+                       uint16_t* act, uint16_t* yd, void* ws, size_t ws_bytes, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if (!xd || !w1 || !w2 || !act || !yd || !ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  GemmArgs g;
+  g.xd = xd;
+  g.w1 = w1;
+  g.w2 = w2;
+  g.act = act;
+  g.yd = yd;
+  g.hdr = at<int32_t>(ws, L.header);
+  g.tasks = at<int32_t>(ws, L.tasks);
+  g.mb_expert = at<int32_t>(ws, L.mblk_expert);
+  g.mb_row0 = at<int32_t>(ws, L.mblk_row0);
+  g.mb_rows = at<int32_t>(ws, L.mblk_rows);
+  g.mb_ready = at<int32_t>(ws, L.mblk_ready);
+  g.R = cfg->T * cfg->k;
+  g.H = cfg->H;
+  g.I = cfg->I;
+  g.E = cfg->E;
+  g.n1 = L.n1_tiles;
+  g.max_tasks = L.max_tasks;
+  g.max_mblk = L.max_mblk;
+  g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
+  g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_forward_reset(g.hdr, g.mb_ready, L.max_mblk, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm(g, L.tile_m, cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd, uint16_t* out,
+                       void* stream) {
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!rt || !rt->pos || !rt->topk_w || !yd || !out) return MOE_ERR_INVALID_ARG;
+  if (launch_combine(rt->pos, rt->topk_w, yd, out, cfg->T, cfg->H, cfg->k, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status moe_status_read(const void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < HDR_SLOTS * 4) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  int32_t code = 0;
+  if (hipMemcpy(&code, ws, sizeof(code), hipMemcpyDeviceToHost) != hipSuccess) return MOE_ERR_HIP;
+  return code == 0 ? MOE_OK : (moe_status)code;
+}
+
+}  // extern "C"

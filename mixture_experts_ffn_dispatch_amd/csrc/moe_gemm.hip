@@ -1,0 +1,282 @@
+// Persistent grouped GEMM of libmoe (gfx950): every expert's Linear-1 with a fused SwiGLU
+// epilogue and its Linear-2, as one launch that walks the tile list moe_plan wrote.
+//
+// X-Stage paper, Introduction: each expert evaluates Linear-1 (H -> 2I), SwiGLU, Linear-2
+// (I -> H); MegaMoE runs these stages inside one persistent kernel, grouped into expert waves,
+// and Section 4.2 reorders independent Linear-1 / Linear-2 tiles across waves. Here:
+//
+//  * A workgroup (4 wavefronts) takes the next tile from the list with one atomic increment,
+//    so tiles start in list order whatever the grid size.
+//  * Linear-1 tile (expert e, m-block, n-tile): 128 gate rows + the matching 128 up rows of
+//    W1[e] against up to tile_m dispatched rows; the epilogue forms
+//    A = bf16(silu(gate) * up) for 128 columns and releases the m-block's ready counter.
+//  * Linear-2 tile: waits (bounded) until all Linear-1 tiles of its m-block have released,
+//    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
+//  * The MFMA A operand is the weight tile and the B operand the token tile, so one lane
+//    ends with four consecutive output columns of one token row (8-byte stores).
+//  * Operands are staged through LDS in 64-wide K steps, double buffered, rows swizzled by
+//    XOR of the 16-byte chunk index with the row's low 3 bits (conflict-free 128-bit reads).
+//  * Every output element accumulates its K products in the same order (ascending K steps of
+//    16 inside one v_mfma_f32_32x32x16_bf16 chain), so tile order, grid size and tile height
+//    never change a result bit.
+//  * Loads and stores use buffer resources bounded to the m-block's rows and the expert's
+//    weight slab: rows past the end read as zero and are never stored.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+__device__ inline unsigned pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return (unsigned)__builtin_bit_cast(unsigned short, a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+__device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+template <int BM, int WN, int WM, int MINW>
+__global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) {
+  constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
+  constexpr int BK = kTileK;
+  constexpr int FN = BN / WN / 32;  // 32x32 MFMA blocks per wave along weight rows
+  constexpr int FM = BM / WM / 32;  // ... along token rows
+  constexpr int ROWS = BN + BM;     // LDS rows per stage: weights first, then tokens
+  constexpr int STAGE = ROWS * BK;  // bf16 elements per stage
+  constexpr int LD = ROWS / 32;     // 16-byte chunks each thread stages per K step
+  static_assert(FN % 2 == 0 && FN >= 2 && FM >= 1, "tile shape");
+  static_assert(WN * WM == 4, "four wavefronts");
+  static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ int s_task;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WN, wm = wave / WN;
+  const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within a 32-row group, chunk
+  const int lds_pchunk = lchunk ^ (lrow & 7);   // swizzled chunk (row & 7 == lrow & 7)
+  const int fr_row = lane & 31, fr_chunk = lane >> 5;
+
+  const uint32_t yd_bytes = (uint32_t)((size_t)p.R * p.H * 2);
+  const uint32_t act_bytes = (uint32_t)((size_t)p.R * p.I * 2);
+  const __amdgpu_buffer_rsrc_t r_yd = make_rsrc(p.yd, yd_bytes);
+  const __amdgpu_buffer_rsrc_t r_act = make_rsrc(p.act, act_bytes);
+
+  for (;;) {
+    if (tid == 0) {
+      const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
+      const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
+      s_task = t < ntasks ? p.tasks[t] : kNoTask;
+    }
+    __syncthreads();
+    // the task and its m-block record are the same for the whole workgroup: keep them scalar
+    const int task = __builtin_amdgcn_readfirstlane(s_task);
+    if (task == kNoTask) break;
+    const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
+    const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
+    const int nt = task & kTaskNtMask;
+    const int e = __builtin_amdgcn_readfirstlane(p.mb_expert[mb]);
+    const int row0 = __builtin_amdgcn_readfirstlane(p.mb_row0[mb]);
+    const int nrows = __builtin_amdgcn_readfirstlane(p.mb_rows[mb]);
+    // a plan this workspace could not have produced: skip the tile, report, never fault
+    if (mb >= p.max_mblk || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
+        nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1)) {
+      if (tid == 0) atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
+      __syncthreads();
+      continue;
+    }
+    const int K = l2 ? p.I : p.H;
+
+    if (l2) {
+      if (tid == 0) {
+        const int need = p.n1 + p.force_timeout;
+        int spins = 0;
+        while (__hip_atomic_load(&p.mb_ready[mb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++spins > p.spin_limit) {
+            atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_TIMEOUT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
+      __syncthreads();
+    }
+
+    // operand buffers bounded to this expert's weight slab and this m-block's rows
+    __amdgpu_buffer_rsrc_t r_w, r_t;
+    if (l2) {
+      r_w = make_rsrc(p.w2 + (size_t)e * p.H * p.I, (uint32_t)((size_t)p.H * p.I * 2));
+      r_t = make_rsrc(p.act + (size_t)row0 * p.I, (uint32_t)((size_t)nrows * p.I * 2));
+    } else {
+      r_w = make_rsrc(p.w1 + (size_t)e * 2 * p.I * p.H, (uint32_t)((size_t)2 * p.I * p.H * 2));
+      r_t = make_rsrc(p.xd + (size_t)row0 * p.H, (uint32_t)((size_t)nrows * p.H * 2));
+    }
+    // staged chunk i of this thread: weight rows for i < BN/32, token rows after; the per-lane
+    // part of the byte offset is one of two bases, the rest is wave-uniform (scalar offset)
+    const uint32_t rowb = (uint32_t)K * 2u;  // bytes per operand row
+    const uint32_t vbase_w = (uint32_t)((l2 ? nt * kTileN2 : nt * kTileN1) + lrow) * rowb + (uint32_t)lchunk * 16u;
+    const uint32_t vbase_t = (uint32_t)lrow * rowb + (uint32_t)lchunk * 16u;
+    const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
+    auto chunk_soff = [&](int i) -> uint32_t {
+      if (i < BN / 32) {
+        if (l2) return (uint32_t)i * 32u * rowb;
+        return i < BN / 64 ? (uint32_t)i * 32u * rowb : up_off + (uint32_t)(i - BN / 64) * 32u * rowb;
+      }
+      return (uint32_t)(i - BN / 32) * 32u * rowb;
+    };
+
+    f32x16 acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    // LDS row of each weight fragment (Linear-1: first half gate, second half the matching up)
+    int wrow[FN];
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      if (l2) wrow[f] = wn * (BN / WN) + f * 32;
+      else
+        wrow[f] = (f < FN / 2) ? wn * (BN / 2 / WN) + f * 32 : BN / 2 + wn * (BN / 2 / WN) + (f - FN / 2) * 32;
+    }
+
+    u32x4 stage_regs[LD];
+    auto load_k = [&](int kt) {
+#pragma unroll
+      for (int i = 0; i < LD; ++i) {
+        stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(i < BN / 32 ? r_w : r_t, (int)(i < BN / 32 ? vbase_w : vbase_t),
+                                                              (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
+      }
+    };
+    auto store_lds = [&](int st) {
+#pragma unroll
+      for (int i = 0; i < LD; ++i) {
+        const int r = lrow + 32 * i;
+        *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[i];
+      }
+    };
+    auto compute = [&](int st) {
+      const uint16_t* base = &lds[st * STAGE];
+#pragma unroll
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const int pc = ((2 * ks + fr_chunk) ^ (fr_row & 7)) * 8;
+        bf16x8 af[FN], bfr[FM];
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          af[f] = *reinterpret_cast<const bf16x8*>(base + (wrow[f] + fr_row) * BK + pc);
+#pragma unroll
+        for (int m = 0; m < FM; ++m)
+          bfr[m] = *reinterpret_cast<const bf16x8*>(base + (BN + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int m = 0; m < FM; ++m)
+            acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f], bfr[m], acc[f][m], 0, 0, 0);
+      }
+    };
+
+    const int KT = K / BK;
+    load_k(0);
+    store_lds(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) load_k(kt + 1);
+      compute(kt & 1);
+      if (kt + 1 < KT) store_lds((kt + 1) & 1);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds, for output block (f, m), rows 8g + 4*(lane>>5) + {0..3} of the
+    // weight fragment (output columns) at token column lane & 31
+#pragma unroll
+    for (int m = 0; m < FM; ++m) {
+      const int tok = wm * (BM / WM) + m * 32 + fr_row;
+      if (tok >= nrows) continue;
+      const uint32_t grow = (uint32_t)(row0 + tok);
+      if (l2) {
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = nt * kTileN2 + wn * (BN / WN) + f * 32 + g * 8 + fr_chunk * 4;
+            if (n < p.H) {
+              u32x2 v;
+              v.x = pack_bf16(acc[f][m][4 * g + 0], acc[f][m][4 * g + 1]);
+              v.y = pack_bf16(acc[f][m][4 * g + 2], acc[f][m][4 * g + 3]);
+              __builtin_amdgcn_raw_buffer_store_b64(v, r_yd, (int)((grow * (uint32_t)p.H + (uint32_t)n) * 2u), 0, 0);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN / 2; ++f)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = nt * kTileN1 + wn * (BN / 2 / WN) + f * 32 + g * 8 + fr_chunk * 4;
+            if (n < p.I) {
+              float a4[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) a4[q] = silu(acc[f][m][4 * g + q]) * acc[f + FN / 2][m][4 * g + q];
+              u32x2 v;
+              v.x = pack_bf16(a4[0], a4[1]);
+              v.y = pack_bf16(a4[2], a4[3]);
+              __builtin_amdgcn_raw_buffer_store_b64(v, r_act, (int)((grow * (uint32_t)p.I + (uint32_t)n) * 2u), 0, 0);
+            }
+          }
+      }
+    }
+
+    if (!l2) {
+      // publish this tile's A columns: every wavefront drains its own stores first (a
+      // workgroup barrier alone does not wait for them), then one lane releases at agent scope
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(&p.mb_ready[mb], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+}
+
+template <int BM, int WN, int WM, int MINW>
+hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
+  int grid = num_workgroups;
+  if (grid <= 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
+    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+    if (err != hipSuccess) return err;
+    grid = cus * (per_cu > 0 ? per_cu : 1);
+  }
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
+  switch (tile_m) {
+    case 256: return launch_variant<256, 2, 2, 1>(a, num_workgroups, s);
+    case 128: return launch_variant<128, 2, 2, 1>(a, num_workgroups, s);
+    case 64: return launch_variant<64, 4, 1, 2>(a, num_workgroups, s);
+    case 32: return launch_variant<32, 4, 1, 2>(a, num_workgroups, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace moe

@@ -1,0 +1,97 @@
+// Internal declarations shared by the libmoe translation units (host and device side).
+// Not part of the public ABI; the public contract is include/moe.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// Workspace header slots (int32).
+enum : int {
+  HDR_ERROR = 0,   // device-side error code (0 or MOE_ERR_TIMEOUT)
+  HDR_CURSOR = 1,  // next task index handed to a persistent workgroup
+  HDR_NTASKS = 2,  // tasks in the list
+  HDR_NMBLK = 3,   // m-blocks in the table
+  HDR_TILE_M = 4,
+  HDR_N1 = 5,
+  HDR_N2 = 6,
+  HDR_SLOTS = 16
+};
+
+constexpr int kTokensPerChunk = 64;  // routing histogram granularity (tokens)
+constexpr int kTileN2 = 256;         // Linear-2 tile: Yd columns
+constexpr int kTileN1 = 128;         // Linear-1 tile: A columns (=> 128 gate + 128 up weight rows)
+constexpr int kTileK = 64;           // K step staged through LDS
+constexpr int kTaskL2Bit = 31;
+constexpr int kTaskMblkShift = 12;
+constexpr int kTaskMblkBits = 19;
+constexpr int kTaskNtMask = 0xFFF;
+constexpr int kDefaultSpinLimit = 1 << 22;
+// "no more tiles": all ones. Never a real task because m-block 0x7FFFF is out of range
+// (the host rejects plans with 2^19 - 1 or more m-blocks).
+constexpr int32_t kNoTask = -1;
+
+// Task word: bit 31 = Linear-2, bits 30..12 = m-block, bits 11..0 = n-tile.
+__host__ __device__ inline int32_t make_task(int l2, int mblk, int nt) {
+  return (int32_t)(((uint32_t)l2 << kTaskL2Bit) | ((uint32_t)mblk << kTaskMblkShift) | (uint32_t)nt);
+}
+
+struct PlanArgs {
+  const float* logits;
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  int32_t* hdr;
+  int32_t* chunk_counts;  // [E][chunks]
+  int32_t* mb_expert;
+  int32_t* mb_row0;
+  int32_t* mb_rows;
+  int32_t* mb_ready;
+  int32_t* tasks;
+  int T, E, k, chunks;
+  int W;         // experts per wave
+  int schedule;  // MOE_SCHED_*
+  int lead;      // interleave lead (>= 1)
+  int tile_m, n1, n2;
+};
+
+struct GemmArgs {
+  const uint16_t* xd;
+  const uint16_t* w1;
+  const uint16_t* w2;
+  uint16_t* act;
+  uint16_t* yd;
+  int32_t* hdr;
+  const int32_t* tasks;
+  const int32_t* mb_expert;
+  const int32_t* mb_row0;
+  const int32_t* mb_rows;
+  int32_t* mb_ready;
+  int R;  // dispatched rows T*k
+  int H, I, E;
+  int n1;  // Linear-1 n-tiles per m-block (the dependency target)
+  int max_tasks, max_mblk;  // capacity of the workspace arrays (guards against a stale plan)
+  int spin_limit;
+  int force_timeout;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s);
+hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s);
+hipError_t launch_scatter(const PlanArgs& a, hipStream_t s);
+hipError_t launch_dispatch(const int32_t* perm, const uint16_t* x, uint16_t* xd, int R, int H, int k,
+                           hipStream_t s);
+hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
+                          int H, int k, hipStream_t s);
+hipError_t launch_forward_reset(int32_t* hdr, int32_t* mb_ready, int max_mblk, hipStream_t s);
+// Persistent grouped GEMM; grid = num_workgroups (0 = CUs x occupancy).
+hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s);
+
+}  // namespace moe

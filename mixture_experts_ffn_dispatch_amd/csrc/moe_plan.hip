@@ -1,0 +1,403 @@
+// Routing and planning kernels of libmoe (gfx950).
+//
+// The layer's router picks k experts per token and Dispatch groups every token's copies by
+// expert (X-Stage paper, Introduction, MoE-layer paragraph); the expert-wave paragraph and
+// Section 4.2 (MegaMoE) fix the tile orders that the schedule builder writes.
+//
+//   route_hist     one wavefront per token: top-k over the E logits (descending, ties to the
+//                  lower expert id), renormalised softmax weights, and a per-(expert, chunk)
+//                  count of the routed slots (LDS atomics on integers: order-free, exact).
+//   scan_schedule  one workgroup: exclusive scan of the expert-major count table, which gives
+//                  every (expert, chunk) its first dispatched row, the expert offsets, the
+//                  m-block table, zeroed dependency counters and the tile list.
+//   scatter        one wavefront per chunk: stable ranks of the chunk's slots inside their
+//                  expert (ballot/match over 64 slots at a time), perm and pos.
+#include <math.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ inline bool ranks_before(float av, int ae, float bv, int be) {
+  // (logit descending, expert id ascending); -0 == +0 as IEEE comparison says
+  return av > bv || (av == bv && ae < be);
+}
+
+template <int R>  // logits held per lane: experts lane, lane + 64, ..., E <= 64 * R
+__global__ __launch_bounds__(256) void route_hist_kernel(PlanArgs a) {
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x;
+  for (int e = tid; e < a.E; e += 256) cnt[e] = 0;
+  __syncthreads();
+
+  const int t_end = min(a.T, (chunk + 1) * kTokensPerChunk);
+  for (int t = chunk * kTokensPerChunk + wave; t < t_end; t += 4) {
+    const float* row = a.logits + (size_t)t * a.E;
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int e = lane + 64 * r;
+      const float x = e < a.E ? row[e] : -INFINITY;
+      v[r] = (x != x) ? -INFINITY : x;  // NaN is not a valid logit; keep selection in range
+    }
+    unsigned taken = 0;
+    float my_v = 0.f, top = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < a.k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int e = lane + 64 * r;
+        if (e < a.E && !((taken >> r) & 1u) && ranks_before(v[r], e, bv, be)) {
+          bv = v[r];
+          be = e;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oe = __shfl_xor(be, off);
+        if (ranks_before(ov, oe, bv, be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      // every lane now holds the same winner (a strict total order has one maximum)
+      if ((be & 63) == lane) taken |= 1u << (be >> 6);
+      if (lane == j) {
+        my_v = bv;
+        my_e = be;
+      }
+      if (j == 0) top = bv;
+    }
+    // softmax restricted to the kept logits; the full denominator cancels
+    const float ex = lane < a.k ? expf(my_v - top) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);  // same on every lane
+    if (lane < a.k) {
+      const size_t f = (size_t)t * a.k + lane;
+      a.topk_ids[f] = my_e;
+      a.topk_w[f] = ex / sum;
+      atomicAdd(&cnt[my_e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += 256) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
+}
+
+constexpr int kScanThreads = 1024;
+
+// Exclusive scan of one int per thread over a 1024-thread workgroup; `total` gets the sum.
+__device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_tmp[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kScanThreads / 64 ? s_tmp[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(w, off);
+      if (lane >= off) w += y;
+    }
+    if (lane < kScanThreads / 64) s_tmp[lane] = w;
+  }
+  __syncthreads();
+  const int base = wave ? s_tmp[wave - 1] : 0;
+  total = s_tmp[kScanThreads / 64 - 1];
+  __syncthreads();  // s_tmp may be reused by the next call
+  return base + x - v;
+}
+
+__global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a) {
+  __shared__ int s_tmp[32];
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];  // expert offsets
+  __shared__ int s_mb[MOE_MAX_EXPERTS + 1];   // first m-block of each expert
+  __shared__ int s_l1s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-1 run
+  __shared__ int s_l2s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-2 run
+  __shared__ int s_a[MOE_MAX_EXPERTS];        // Linear-1 tiles per wave
+  __shared__ int s_b[MOE_MAX_EXPERTS];        // Linear-2 tiles per wave
+  const int tid = threadIdx.x;
+  const int E = a.E, BM = a.tile_m;
+
+  // 1. exclusive scan of the expert-major (expert, chunk) count table, in place: entry
+  //    (e, c) becomes the first dispatched row of chunk c's slots routed to expert e
+  constexpr int IT = 8;
+  const int n = E * a.chunks;
+  int carry = 0;
+  for (int base = 0; base < n; base += kScanThreads * IT) {
+    int vals[IT];
+    int sum = 0;
+    const int i0 = base + tid * IT;
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      vals[i] = i0 + i < n ? a.chunk_counts[i0 + i] : 0;
+      sum += vals[i];
+    }
+    int tot;
+    int run = carry + block_exclusive_scan(sum, s_tmp, tot);
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int idx = i0 + i;
+      if (idx < n) {
+        a.chunk_counts[idx] = run;
+        if (idx % a.chunks == 0) s_off[idx / a.chunks] = run;
+      }
+      run += vals[i];
+    }
+    carry += tot;
+  }
+  if (tid == 0) s_off[E] = carry;  // = T * k
+  __syncthreads();
+
+  // 2. counts, offsets and the m-block table
+  for (int e = tid; e <= E; e += kScanThreads) a.offsets[e] = s_off[e];
+  int cnt = 0, nmb = 0;
+  if (tid < E) {
+    cnt = s_off[tid + 1] - s_off[tid];
+    nmb = (cnt + BM - 1) / BM;
+    a.counts[tid] = cnt;
+  }
+  int total_mb;
+  const int mb0 = block_exclusive_scan(nmb, s_tmp, total_mb);
+  if (tid < E) s_mb[tid] = mb0;
+  if (tid == 0) s_mb[E] = total_mb;
+  if (tid < E) {
+    for (int i = 0; i < nmb; ++i) {
+      a.mb_expert[mb0 + i] = tid;
+      a.mb_row0[mb0 + i] = s_off[tid] + i * BM;
+      a.mb_rows[mb0 + i] = min(BM, cnt - i * BM);
+    }
+  }
+  for (int i = tid; i < total_mb; i += kScanThreads) a.mb_ready[i] = 0;
+  __syncthreads();
+
+  // 3. tile counts per expert wave and where each wave's runs start in the list
+  const int W = a.W, nw = (E + W - 1) / W, D = a.lead;
+  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  int aw = 0, bw = 0;
+  if (tid < nw) {
+    const int m = s_mb[min(E, (tid + 1) * W)] - s_mb[tid * W];
+    aw = m * a.n1;
+    bw = m * a.n2;
+    s_a[tid] = aw;
+    s_b[tid] = bw;
+  }
+  __syncthreads();
+  int unused;
+  if (!interleaved) {
+    // Expert-Wave order: L1(0) L2(0) L1(1) L2(1) ...
+    const int st = block_exclusive_scan(aw + bw, s_tmp, unused);
+    if (tid < nw) {
+      s_l1s[tid] = st;
+      s_l2s[tid] = st + aw;
+    }
+  } else {
+    // interleaved: L1(0) .. L1(D-1), then segment i = L2(i) merged with L1(i + D)
+    int prefix_total;
+    const int p = block_exclusive_scan(tid < min(D, nw) ? aw : 0, s_tmp, prefix_total);
+    const int seg = tid < nw ? bw + (tid + D < nw ? s_a[tid + D] : 0) : 0;
+    const int q = prefix_total + block_exclusive_scan(seg, s_tmp, unused);
+    if (tid < nw) {
+      s_l2s[tid] = q;                      // segment tid starts with L2(tid)
+      if (tid < D) s_l1s[tid] = p;         // lead prefix
+      if (tid + D < nw) s_l1s[tid + D] = q;  // L1(tid + D) lives in segment tid
+    }
+  }
+  __syncthreads();
+
+  // 4. write the tile list; within a run tiles go (expert, m-block, n-tile)
+  for (int w = 0; w < nw; ++w) {
+    const int mbw0 = s_mb[w * W];
+    const int a_w = s_a[w], b_w = s_b[w];
+    // Linear-1 tiles of wave w
+    const int b_seg = (interleaved && w >= D) ? s_b[w - D] : -1;  // L2 run it is spread over
+    for (int q = tid; q < a_w; q += kScanThreads) {
+      long long at = s_l1s[w] + q;
+      if (b_seg > 0) {
+        // emitted right after L2 tile number ceil((q+1) * b / a) of its segment
+        at += ((long long)(q + 1) * b_seg + a_w - 1) / a_w;
+      }
+      a.tasks[at] = make_task(0, mbw0 + q / a.n1, q % a.n1);
+    }
+    // Linear-2 tiles of wave w
+    const int a_seg = (interleaved && w + D < nw) ? s_a[w + D] : 0;  // L1 tiles spread over it
+    for (int j = tid; j < b_w; j += kScanThreads) {
+      long long at = s_l2s[w] + j;
+      if (a_seg > 0) at += (long long)j * a_seg / b_w;  // L1 tiles emitted before L2 tile j
+      a.tasks[at] = make_task(1, mbw0 + j / a.n2, j % a.n2);
+    }
+  }
+  if (tid == 0) {
+    a.hdr[HDR_ERROR] = 0;
+    a.hdr[HDR_CURSOR] = 0;
+    a.hdr[HDR_NTASKS] = total_mb * (a.n1 + a.n2);
+    a.hdr[HDR_NMBLK] = total_mb;
+    a.hdr[HDR_TILE_M] = BM;
+    a.hdr[HDR_N1] = a.n1;
+    a.hdr[HDR_N2] = a.n2;
+  }
+}
+
+__global__ __launch_bounds__(64) void scatter_kernel(PlanArgs a) {
+  __shared__ int run[MOE_MAX_EXPERTS];
+  const int lane = threadIdx.x, chunk = blockIdx.x;
+  for (int e = lane; e < a.E; e += 64) run[e] = a.chunk_counts[(size_t)e * a.chunks + chunk];
+  __syncthreads();
+  const int R = a.T * a.k;
+  const int f0 = chunk * kTokensPerChunk * a.k;
+  const int f1 = min(R, f0 + kTokensPerChunk * a.k);
+  for (int s = f0; s < f1; s += 64) {
+    const int f = s + lane;
+    const bool valid = f < f1;
+    int e = valid ? a.topk_ids[f] : -1;
+    if ((unsigned)e >= (unsigned)a.E) e = -1;
+    unsigned long long remaining = __ballot(e >= 0);
+    int row = -1;
+    while (remaining) {
+      const int leader = __ffsll((long long)remaining) - 1;
+      const int ev = __shfl(e, leader);
+      const unsigned long long m = __ballot(e == ev) & remaining;
+      const int base = run[ev];
+      if (e == ev) row = base + __popcll(m & ((1ull << lane) - 1ull));
+      if (lane == leader) run[ev] = base + __popcll(m);
+      remaining &= ~m;
+    }
+    if (e >= 0 && (unsigned)row < (unsigned)R) {
+      a.perm[row] = f;
+      a.pos[f] = row;
+    }
+  }
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* perm, const uint16_t* x,
+                                                       uint16_t* xd, int R, int H, int k, int T) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cpr = H / 8;  // 16-byte chunks per row
+  for (int r = blockIdx.x * 4 + wave; r < R; r += gridDim.x * 4) {
+    const int t = perm[r] / k;
+    if ((unsigned)t >= (unsigned)T) continue;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
+    u32x4* dst = reinterpret_cast<u32x4*>(xd + (size_t)r * H);
+    for (int c = lane; c < cpr; c += 64) dst[c] = src[c];
+  }
+}
+
+__device__ inline float bf16_lo(unsigned v) { return __uint_as_float(v << 16); }
+__device__ inline float bf16_hi(unsigned v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ inline unsigned pack_bf16(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (unsigned)__builtin_bit_cast(unsigned short, a) |
+         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
+}
+
+__global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const float* w,
+                                                      const uint16_t* yd, uint16_t* out, int T,
+                                                      int H, int k, int R) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cpr = H / 8;
+  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
+    const int32_t* pt = pos + (size_t)t * k;
+    const float* wt = w + (size_t)t * k;
+    for (int c = lane; c < cpr; c += 64) {
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      for (int j = 0; j < k; ++j) {  // fixed ascending order
+        const int r = pt[j];
+        if ((unsigned)r >= (unsigned)R) continue;
+        const float wj = wt[j];
+        const u32x4 v = reinterpret_cast<const u32x4*>(yd + (size_t)r * H)[c];
+        acc[0] = fmaf(wj, bf16_lo(v.x), acc[0]);
+        acc[1] = fmaf(wj, bf16_hi(v.x), acc[1]);
+        acc[2] = fmaf(wj, bf16_lo(v.y), acc[2]);
+        acc[3] = fmaf(wj, bf16_hi(v.y), acc[3]);
+        acc[4] = fmaf(wj, bf16_lo(v.z), acc[4]);
+        acc[5] = fmaf(wj, bf16_hi(v.z), acc[5]);
+        acc[6] = fmaf(wj, bf16_lo(v.w), acc[6]);
+        acc[7] = fmaf(wj, bf16_hi(v.w), acc[7]);
+      }
+      u32x4 o;
+      o.x = pack_bf16(acc[0], acc[1]);
+      o.y = pack_bf16(acc[2], acc[3]);
+      o.z = pack_bf16(acc[4], acc[5]);
+      o.w = pack_bf16(acc[6], acc[7]);
+      reinterpret_cast<u32x4*>(out + (size_t)t * H)[c] = o;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void forward_reset_kernel(int32_t* hdr, int32_t* mb_ready,
+                                                            int max_mblk) {
+  const int n = min(hdr[HDR_NMBLK], max_mblk);
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    mb_ready[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    hdr[HDR_CURSOR] = 0;
+    hdr[HDR_ERROR] = 0;
+  }
+}
+
+inline int grid_rows(long long rows_per_block_units) {
+  long long g = rows_per_block_units;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s) {
+  const int R = (a.E + 63) / 64;
+  const dim3 grid(a.chunks), block(256);
+  if (R <= 1) hipLaunchKernelGGL(route_hist_kernel<1>, grid, block, 0, s, a);
+  else if (R <= 2) hipLaunchKernelGGL(route_hist_kernel<2>, grid, block, 0, s, a);
+  else if (R <= 4) hipLaunchKernelGGL(route_hist_kernel<4>, grid, block, 0, s, a);
+  else if (R <= 8) hipLaunchKernelGGL(route_hist_kernel<8>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(route_hist_kernel<16>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(scan_schedule_kernel, dim3(1), dim3(kScanThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const PlanArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(scatter_kernel, dim3(a.chunks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const int32_t* perm, const uint16_t* x, uint16_t* xd, int R, int H, int k,
+                           hipStream_t s) {
+  const int T = R / k;
+  hipLaunchKernelGGL(dispatch_kernel, dim3(grid_rows((R + 3) / 4)), dim3(256), 0, s, perm, x, xd, R, H,
+                     k, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
+                          int H, int k, hipStream_t s) {
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, w, yd, out, T,
+                     H, k, T * k);
+  return hipGetLastError();
+}
+
+hipError_t launch_forward_reset(int32_t* hdr, int32_t* mb_ready, int max_mblk, hipStream_t s) {
+  const int blocks = max(1, min(64, (max_mblk + 255) / 256));
+  hipLaunchKernelGGL(forward_reset_kernel, dim3(blocks), dim3(256), 0, s, hdr, mb_ready, max_mblk);
+  return hipGetLastError();
+}
+
+}  // namespace moe

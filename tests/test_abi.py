@@ -1,0 +1,105 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, and the
+host-only calls (layout, validation) behave as the header says. No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_dispatch_amd as moe
+from mixture_experts_ffn_dispatch_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.load()
+    names = declared_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert moe.abi_version() == 1
+
+
+def test_strerror():
+    for code in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(moe.strerror(code), str) and moe.strerror(code)
+
+
+def _cfg(**kw):
+    base = dict(T=4096, H=7168, I=2048, E=32, k=8, experts_per_wave=4)
+    base.update(kw)
+    return moe.MoeConfig(**base)
+
+
+def test_layout_is_consistent():
+    L = moe.moe_workspace_layout(_cfg())
+    assert L["tile_m"] == 256 and L["n1_tiles"] == 16 and L["n2_tiles"] == 28
+    assert L["chunks"] == 64
+    # max m-blocks: every row of every active expert fills tiles, plus one partial per expert
+    assert L["max_mblk"] == (4096 * 8 + 32 * 255) // 256
+    assert L["max_tasks"] == L["max_mblk"] * (16 + 28)
+    offs = [L[n] for n in ("header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready", "tasks")]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L["total_bytes"] >= L["tasks"] + 4 * L["max_tasks"]
+    assert moe.moe_workspace_size(_cfg()) == L["total_bytes"]
+
+
+@pytest.mark.parametrize("T,k,E,tile", [(4096, 8, 32, 256), (8192, 8, 128, 128), (512, 6, 64, 64),
+                                         (65536, 2, 16, 256), (256, 2, 8, 64), (8, 1, 64, 32)])
+def test_auto_tile_height(T, k, E, tile):
+    assert moe.moe_workspace_layout(_cfg(T=T, k=k, E=E))["tile_m"] == tile
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(k=33, E=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(k=9, E=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(E=1025, k=2), moe.MOE_ERR_UNSUPPORTED),
+    (dict(H=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(I=96), moe.MOE_ERR_UNSUPPORTED),
+    (dict(experts_per_wave=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(schedule=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(lead_waves=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(tile_m=48), moe.MOE_ERR_UNSUPPORTED),
+    (dict(flags=4), moe.MOE_ERR_INVALID_ARG),
+    (dict(reserved=(0, 1, 0, 0)), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 20, H=8192, k=8, E=64), moe.MOE_ERR_UNSUPPORTED),  # row buffers past 4 GiB
+])
+def test_invalid_configs_rejected(kw, code):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(_cfg(**kw))
+    assert ei.value.status == code
+
+
+def test_null_pointers_rejected_before_any_launch():
+    lib = moe.load()
+    c = _cfg().to_c()
+    rt = _lib.CRouting()
+    # a valid config with missing pointers must fail on the host, touching no device
+    assert lib.moe_plan(ctypes.byref(c), None, ctypes.byref(rt), None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch(ctypes.byref(c), ctypes.byref(rt), None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward(ctypes.byref(c), None, None, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(c), ctypes.byref(rt), None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_status_read(None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size(None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_workspace_size(ctypes.byref(c), None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_undersized_workspace_rejected():
+    lib = moe.load()
+    c = _cfg().to_c()
+    need = moe.moe_workspace_size(_cfg())
+    rt = _lib.CRouting(*([1 << 20] * 6))  # non-null dummies: the size check comes first
+    dummy = 1 << 20
+    assert lib.moe_plan(ctypes.byref(c), dummy, ctypes.byref(rt), dummy, need - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_forward(ctypes.byref(c), dummy, dummy, dummy, dummy, dummy, dummy, need - 1, None) == \
+        moe.MOE_ERR_WORKSPACE

@@ -1,0 +1,134 @@
+"""GPU parity against the CPU oracle through the C ABI (MI355X).
+
+Bars: routing ids, counts, offsets, perm, pos and the dispatched rows bit-exact; router
+weights within 2^-20; A, Yd (per expert) and the layer output within
+max|gpu - ref| <= 1e-2 * max|ref|; the exact-integer case bit-exact end to end.
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+from oracle import invariants as V, moe_ref as R
+from tests.gpu_util import Device, assert_close_rel, dev_bf16, fetch, host_bits, make_cfg, note, run
+
+import mixture_experts_ffn_dispatch_amd as moe
+
+pytestmark = pytest.mark.gpu
+
+
+def check_routing(g, o):
+    np.testing.assert_array_equal(g["topk_ids"], o["ids"])
+    np.testing.assert_allclose(g["topk_w"], o["w"], rtol=0, atol=2.0 ** -20)
+    np.testing.assert_array_equal(g["counts"], o["counts"])
+    np.testing.assert_array_equal(g["offsets"], o["offsets"])
+    np.testing.assert_array_equal(g["perm"], o["perm"])
+    np.testing.assert_array_equal(g["pos"], o["pos"])
+
+
+def check_full(g, o, xd_bits, E):
+    check_routing(g, o)
+    np.testing.assert_array_equal(xd_bits, o["xd"])
+    assert_close_rel(g["act"], o["a"], what="A")
+    for e in range(E):
+        lo, hi = o["offsets"][e], o["offsets"][e + 1]
+        if hi > lo:
+            assert_close_rel(g["yd"][lo:hi], o["yd"][lo:hi], what=f"Yd expert {e}")
+    assert_close_rel(g["out"], o["out"], what="out")
+
+
+@pytest.mark.parametrize("k", [1, 2])
+@pytest.mark.parametrize("tile_m", [32, 64, 128, 256])
+@pytest.mark.parametrize("schedule", [moe.MOE_SCHED_EXPERT_WAVE, moe.MOE_SCHED_INTERLEAVED])
+def test_exact_integer_case_bit_exact(k, tile_m, schedule):
+    note(f"exact-integer k={k} tile_m={tile_m} schedule={schedule}")
+    c = V.exact_integer_case(T=100, H=256, I=192, E=4, k=k, seed=3)
+    cfg = moe.MoeConfig(T=100, H=256, I=192, E=4, k=k, experts_per_wave=1, schedule=schedule, tile_m=tile_m)
+    dev = Device(c)
+    b = run(cfg, dev)
+    g = fetch(b)
+    ex = c["expected"]
+    np.testing.assert_array_equal(g["topk_ids"], ex["ids"])
+    np.testing.assert_array_equal(g["topk_w"], ex["w"])
+    T = 100
+    np.testing.assert_array_equal(g["act"][g["pos"]].reshape(T, k, -1), ex["a_tok"])
+    np.testing.assert_array_equal(g["yd"][g["pos"]].reshape(T, k, -1), ex["y_tok"])
+    np.testing.assert_array_equal(g["out"], ex["out"])
+
+
+def test_tiny_workload_full_parity():
+    s = W.shape("tiny")
+    note(f"full parity {W.describe(s)}")
+    d = W.generate(s)
+    o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], s.k)
+    b = run(make_cfg(s), Device(d))
+    check_full(fetch(b), o, host_bits(b["xd"]), s.E)
+
+
+SWEEP = [
+    # T, H, I, E, k, W, tile_m   (ragged T, one expert, k = E, empty experts, N tails, small dims)
+    (1, 64, 64, 1, 1, 1, 0),
+    (37, 64, 64, 1, 1, 1, 32),
+    (130, 192, 320, 5, 2, 2, 0),
+    (257, 128, 64, 4, 4, 1, 64),
+    (65, 320, 192, 16, 3, 3, 32),
+    (300, 256, 384, 12, 1, 5, 128),
+    (96, 64, 128, 64, 8, 8, 32),
+    (200, 512, 256, 33, 5, 4, 256),
+    (513, 128, 192, 3, 3, 1, 0),
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,Wv,tile_m", SWEEP)
+@pytest.mark.parametrize("schedule", [moe.MOE_SCHED_EXPERT_WAVE, moe.MOE_SCHED_INTERLEAVED])
+def test_shape_sweep_full_parity(T, H, I, E, k, Wv, tile_m, schedule):
+    s = W.shape(T=T, H=H, I=I, E=E, k=k, experts_per_wave=Wv, seed=T * 31 + E, x_std=1.0, w_std=0.05)
+    note(f"sweep {W.describe(s)} tile_m={tile_m} schedule={schedule}")
+    d = W.generate(s)
+    if E >= 16:  # leave some experts without rows
+        d["logits"][:, E // 2:] -= 30.0
+    o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], k)
+    cfg = make_cfg(s, tile_m=tile_m, schedule=schedule)
+    b = run(cfg, Device(d))
+    check_full(fetch(b), o, host_bits(b["xd"]), E)
+    if E >= 16:
+        assert (o["counts"] == 0).any()
+
+
+def test_identical_experts_match_dense_ffn():
+    s = W.shape(T=160, H=256, I=128, E=6, k=3, seed=21, x_std=1.0, w_std=0.05)
+    note(f"identical experts {W.describe(s)}")
+    d = W.generate(s)
+    d["w1"], d["w2"] = V.identical_experts(d["x"], d["w1"][0], d["w2"][0], s.E)
+    dense = V.dense_ffn(d["x"], d["w1"][0], d["w2"][0])
+    b = run(make_cfg(s), Device(d))
+    out = fetch(b, keys=("out",))["out"]
+    ref = R.f64_to_bf16_bits(dense["y"])
+    assert_close_rel(out, ref, what="identical experts vs dense FFN")
+
+
+def test_top1_single_expert_matches_dense_ffn():
+    s = W.shape(T=150, H=128, I=256, E=1, k=1, seed=22, x_std=1.0, w_std=0.05)
+    note(f"top-1 E=1 {W.describe(s)}")
+    d = W.generate(s)
+    dense = V.dense_ffn(d["x"], d["w1"][0], d["w2"][0])
+    b = run(make_cfg(s), Device(d))
+    g = fetch(b, keys=("topk_w", "out"))
+    assert np.all(g["topk_w"] == 1.0)
+    assert_close_rel(g["out"], R.f64_to_bf16_bits(dense["y"]), what="E=1 top-1 vs dense FFN")
+
+
+def test_routing_ties_and_signed_zero():
+    # equal logits and -0/+0 must pick the lower expert id first, exactly like the oracle
+    T, E, k = 128, 8, 3
+    lg = np.zeros((T, E), np.float32)
+    lg[1::2] = -0.0
+    lg[::3, 5] = 1.0
+    lg[::5, 2] = -0.0
+    lg[::7] = np.float32(0.5)
+    s = W.shape(T=T, H=64, I=64, E=E, k=k, seed=23)
+    d = W.generate(s, parts=("x", "w1", "w2"))
+    d["logits"] = lg
+    o = R.moe_layer(d["x"], lg, d["w1"], d["w2"], k)
+    b = run(make_cfg(s), Device(d))
+    check_routing(fetch(b), o)
