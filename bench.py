@@ -1,0 +1,257 @@
+"""Benchmark: one GPU's share of the expert-parallel MoE FFN layer on MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_share]
+
+A step is one pass of the whole layer over one batch already resident in HBM: moe_plan
+(route, histogram, scan, scatter, tile list) -> moe_dispatch -> moe_forward (persistent grouped
+GEMM: Linear-1 + SwiGLU, Linear-2) -> moe_combine. W untimed steps, then exactly K timed steps
+bracketed by device synchronisation. Prints ONE JSON line on stdout.
+
+value = layer TFLOP/s = 6*T*k*H*I per step / seconds per step (the two expert GEMMs).
+roofline = the persistent GEMM kernel (the dominant launch): its flops per launch divided by
+its average duration, measured with events on the stream it runs on, against the dense bf16
+MFMA peak of MI355X (2.5 PFLOP/s).
+cpu_baseline = the CPU oracle (float64 NumPy) on a bounded sample of the same workload: the
+first experts' rows (whole experts, in expert order) until about 10 s of work, scaled to
+TFLOP/s by the sample's flops.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(s, counts) -> int:
+    """Bytes the staged layer must move once each: X and logits in, weights of experts with
+    rows, Xd / A / Yd written and read once, the output, and the routing metadata."""
+    R = s.T * s.k
+    active = int((counts > 0).sum())
+    return (s.T * s.H * 2 + s.T * s.E * 4 + active * 3 * s.H * s.I * 2 + 2 * R * s.H * 2 + 2 * R * s.I * 2
+            + 2 * R * s.H * 2 + s.T * s.H * 2 + R * 16)
+
+
+def gemm_bytes(s, counts) -> int:
+    """Algorithmic HBM bytes of one moe_forward launch: Xd read, active experts' W1 and W2
+    read, A written and read back, Yd written."""
+    R = s.T * s.k
+    active = int((counts > 0).sum())
+    return R * s.H * 2 + active * 3 * s.H * s.I * 2 + 2 * R * s.I * 2 + R * s.H * 2
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("moe_gemm.hip", "moe_internal.h"):
+        with open(os.path.join(ROOT, "mixture_experts_ffn_dispatch_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch of the persistent GEMM from committed rocprofv3 counter runs, or
+    None when they are missing or were taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", f"gemm_persistent_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(s, data, budget_s: float = 10.0) -> dict:
+    """Time the CPU oracle on whole experts (in expert order) until the budget is spent."""
+    import numpy as np
+
+    from oracle import moe_ref as R
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    ids, w = R.route(data["logits"], s.k)
+    counts, offsets, perm, pos = R.plan(ids, s.E)
+    t_route = time.perf_counter() - t0
+    rows = 0
+    experts = 0
+    t_ffn = 0.0
+    for e in range(s.E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        xd = R.dispatch(data["x"], perm[lo:hi], s.k)
+        t1 = time.perf_counter()
+        R.expert_ffn(xd, data["w1"][e], data["w2"][e])
+        t_ffn += time.perf_counter() - t1
+        rows += hi - lo
+        experts += 1
+        if t_ffn >= budget_s:
+            break
+    flops = 6.0 * rows * s.H * s.I
+    # routing of the whole batch is charged in proportion to the rows sampled
+    t_total = t_ffn + t_route * rows / (s.T * s.k)
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{experts} of {s.E} experts ({rows} of {s.T * s.k} dispatched rows), float64 NumPy; "
+                      f"routing of all {s.T} tokens charged pro rata; {t_total:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="dsv3_share")
+    ap.add_argument("--schedule", choices=["interleaved", "expert_wave"], default="interleaved")
+    ap.add_argument("--lead", type=int, default=1)
+    ap.add_argument("--tile-m", type=int, default=0)
+    ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU's share of the layer; runs on more than one GPU are not part "
+            "of this build (expert parallelism across GPUs is described, not built). Use --gpus 1.")
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_dispatch_amd as moe
+    import moe_workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    s = W.shape(args.workload)
+    log(f"workload {W.describe(s)}")
+    t0 = time.perf_counter()
+    data = W.generate(s)
+    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, w1, w2 = dev(data["x"]), dev(data["w1"]), dev(data["w2"])
+    logits = torch.from_numpy(data["logits"]).cuda()
+    sched = {"interleaved": moe.MOE_SCHED_INTERLEAVED, "expert_wave": moe.MOE_SCHED_EXPERT_WAVE}
+
+    def make_cfg(name):
+        return moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
+                             schedule=sched[name], lead_waves=args.lead, tile_m=args.tile_m,
+                             num_workgroups=args.num_workgroups)
+
+    stream = torch.cuda.current_stream()
+
+    def timed(name, steps, warmup):
+        cfg = make_cfg(name)
+        b = moe.alloc_buffers(cfg)
+        for _ in range(warmup):
+            moe.run_layer(cfg, b, x, logits, w1, w2)
+        st = moe.moe_status_read(b["ws"])
+        assert st == moe.MOE_OK, moe.strerror(st)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            e = ev[i]
+            e[0].record(stream)
+            moe.moe_plan(cfg, logits, b, b["ws"])
+            e[1].record(stream)
+            moe.moe_dispatch(cfg, b, x, b["xd"])
+            e[2].record(stream)
+            moe.moe_forward(cfg, b["xd"], w1, w2, b["act"], b["yd"], b["ws"])
+            e[3].record(stream)
+            moe.moe_combine(cfg, b, b["yd"], b["out"])
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        st = moe.moe_status_read(b["ws"])
+        assert st == moe.MOE_OK, moe.strerror(st)
+        per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])  # ms
+        step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
+        counts = b["counts"].cpu().numpy()
+        layout = moe.moe_workspace_layout(cfg)
+        return dict(wall_ms=wall * 1e3 / steps, step_ms=step_ms, per=per, counts=counts, layout=layout)
+
+    main_res = timed(args.schedule, args.steps, args.warmup)
+    other = None
+    if not args.no_compare:
+        oname = "expert_wave" if args.schedule == "interleaved" else "interleaved"
+        other = (oname, timed(oname, args.steps, args.warmup))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    flops = 6.0 * s.T * s.k * s.H * s.I
+    ms = float(main_res["wall_ms"])
+    fwd_ms = float(np.mean(main_res["per"][:, 2]))
+    counts = main_res["counts"]
+    traffic = traffic_from_profiles(args.workload)
+    achieved = flops / (fwd_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "MoE layer TFLOP/s (bf16) and % of MFMA peak; us/layer; HBM GB/s at small M",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
+                   "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "lead_waves": args.lead,
+                   "tile_m": main_res["layout"]["tile_m"], "seed": s.seed},
+        "roofline": {"bound": "mfma", "kernel": "gemm_persistent_kernel", "achieved": round(achieved, 3),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "us_per_layer": round(ms * 1e3, 2),
+        "mfma_frac_layer": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+        "hbm_gbps_algorithmic": round(algorithmic_bytes(s, counts) / (ms * 1e-3) / 1e9, 1),
+        "gemm_hbm_gbps_algorithmic": round(gemm_bytes(s, counts) / (fwd_ms * 1e-3) / 1e9, 1),
+        "per_call_us": {k: round(float(np.mean(main_res["per"][:, j])) * 1e3, 2)
+                        for j, k in enumerate(("plan", "dispatch", "forward", "combine"))},
+        "step_us_median": round(float(np.median(main_res["step_ms"])) * 1e3, 2),
+        "active_experts": int((counts > 0).sum()),
+    }
+    if other is not None:
+        oname, o = other
+        rec["other_schedule"] = {"schedule": oname, "value": round(flops / (o["wall_ms"] * 1e-3) / 1e12, 3),
+                                 "us_per_layer": round(float(o["wall_ms"]) * 1e3, 2),
+                                 "forward_us": round(float(np.mean(o["per"][:, 2])) * 1e3, 2)}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        rec["cpu_baseline"] = cpu_baseline(s, data, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

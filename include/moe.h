@@ -78,7 +78,7 @@ typedef struct moe_config {
   int32_t experts_per_wave; /* W >= 1; wave w holds experts [w*W, min(E, (w+1)*W))              */
   int32_t schedule;         /* MOE_SCHED_*                                                       */
   int32_t lead_waves;       /* interleaved order only: D >= 1 (0 means 1); ignored otherwise    */
-  int32_t num_workgroups;   /* persistent grid size; 0 = one per compute unit per occupancy slot */
+  int32_t num_workgroups;   /* persistent grid; 0 or more than fits at once = every resident slot */
   int32_t tile_m;           /* rows per GEMM tile: 0 = chosen from T*k/E, else 32, 64, 128, 256 */
   int32_t spin_limit;       /* bounded-wait iterations of a Linear-2 tile; 0 = default (~seconds)*/
   int32_t flags;            /* must be 0 except MOE_FLAG_* bits below                            */
@@ -104,16 +104,19 @@ typedef struct moe_routing {
    base; all int32 arrays). Filled on the host by moe_workspace_layout. */
 typedef struct moe_ws_layout {
   size_t total_bytes;   /* = moe_workspace_size                                     */
-  size_t header;        /* int32[16]: [0] error code, [1] task cursor, [2] task count,
+  size_t header;        /* int32[32]: [0] error code, [1] task cursor, [2] task count,
                            [3] m-block count, [4] tile_m, [5] L1 n-tiles per m-block,
-                           [6] L2 n-tiles per m-block                               */
+                           [6] L2 n-tiles per m-block, [7] exited workgroups,
+                           [8..15] tiles taken by each locality group              */
   size_t chunk_counts;  /* int32[E * chunks]: per-(expert, token chunk) counts, then bases */
   size_t mblk_expert;   /* int32[max_mblk]                                        */
   size_t mblk_row0;     /* int32[max_mblk]                                        */
   size_t mblk_rows;     /* int32[max_mblk]                                        */
   size_t mblk_ready;    /* int32[max_mblk]: Linear-1 tiles finished per m-block   */
-  size_t tasks;         /* int32[max_tasks]: bit 31 = Linear-2, bits 30..12 m-block, 11..0 n-tile */
+  size_t tasks;         /* int32[max_tasks]: the tile list in schedule order; bit 31 = Linear-2,
+                           bits 30..12 m-block, bits 11..0 n-tile                    */
   int32_t chunks;       /* token chunks of the routing histogram                  */
+  int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;
   int32_t max_tasks;
   int32_t tile_m;       /* rows per tile                                          */
@@ -152,12 +155,14 @@ moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* layout);
 moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
                     size_t ws_bytes, void* stream);
 
-/* Dispatch: xd[r, :] = x[perm[r] / k, :] for r < T*k (bit copy).
+/* Dispatch: xd[r, :] = x[perm[r] / k, :] for r < T*k (bit copy). Implemented token-major
+ * (each token row is read once and written to its k rows pos[t*k + j]), so it reads rt->pos.
  *   x [T, H] bf16 in; xd [T*k, H] bf16 out (caller-allocated). */
 moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint16_t* x,
                         uint16_t* xd, void* stream);
 
-/* Expert FFN over all dispatched rows in one persistent launch (plus a tiny counter reset).
+/* Expert FFN over all dispatched rows in one persistent launch (its last workgroup resets the
+ * plan's counters, so moe_forward may be repeated on one plan).
  *   xd  [T*k, H] bf16 dispatched rows (from moe_dispatch)
  *   w1  [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up (out x in, like nn.Linear.weight)
  *   w2  [E, H, I] bf16
@@ -177,8 +182,8 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd,
                        uint16_t* out, void* stream);
 
-/* Synchronises `stream`, then returns the device-side error recorded in the workspace by the
- * last moe_plan / moe_forward: MOE_OK, MOE_ERR_TIMEOUT (a bounded wait expired), or
+/* Synchronises `stream`, then returns the device-side error recorded in the workspace since
+ * the last moe_plan: MOE_OK, MOE_ERR_TIMEOUT (a bounded wait expired), or
  * MOE_ERR_WORKSPACE (moe_forward found a tile that no moe_plan for this cfg could have written
  * and skipped it); MOE_ERR_HIP if the stream reports a failure. */
 moe_status moe_status_read(const void* ws, size_t ws_bytes, void* stream);

@@ -45,7 +45,8 @@ class CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
         "tasks")] + [(n, ctypes.c_int32) for n in (
-            "chunks", "max_mblk", "max_tasks", "tile_m", "tile_n1", "tile_n2", "n1_tiles", "n2_tiles")]
+            "chunks", "chunk_tokens", "max_mblk", "max_tasks", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
+            "n2_tiles")]
 
 
 @dataclass

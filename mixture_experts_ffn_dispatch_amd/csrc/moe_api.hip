@@ -48,7 +48,11 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   const int BM = c->tile_m ? c->tile_m : auto_tile_m(*c);
   const long long n1 = (c->I + kTileN1 - 1) / kTileN1;
   const long long n2 = (c->H + kTileN2 - 1) / kTileN2;
-  const long long chunks = ((long long)c->T + kTokensPerChunk - 1) / kTokensPerChunk;
+  // routing histogram granularity: at least 16 tokens per chunk, and at most 32K (expert,
+  // chunk) counts so the single-workgroup scan stays short
+  long long chunk_tokens = ((long long)c->T * c->E + 32767) / 32768;
+  chunk_tokens = chunk_tokens < 16 ? 16 : (chunk_tokens + 15) / 16 * 16;
+  const long long chunks = ((long long)c->T + chunk_tokens - 1) / chunk_tokens;
   const long long active = R < c->E ? R : c->E;
   const long long max_mblk = (R + active * (BM - 1)) / BM;
   const long long max_tasks = max_mblk * (n1 + n2);
@@ -56,6 +60,7 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   if (max_mblk >= (1ll << kTaskMblkBits) - 1) return MOE_ERR_UNSUPPORTED;
   if (max_tasks > 0x7FFFFFFFll || chunks * c->E > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
   L->chunks = (int32_t)chunks;
+  L->chunk_tokens = (int32_t)chunk_tokens;
   L->max_mblk = (int32_t)max_mblk;
   L->max_tasks = (int32_t)max_tasks;
   L->tile_m = BM;
@@ -149,6 +154,7 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.E = cfg->E;
   a.k = cfg->k;
   a.chunks = L.chunks;
+  a.chunk_tokens = L.chunk_tokens;
   a.W = cfg->experts_per_wave > cfg->E ? cfg->E : cfg->experts_per_wave;
   a.schedule = cfg->schedule;
   a.lead = cfg->lead_waves > 0 ? cfg->lead_waves : 1;
@@ -166,9 +172,8 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
                         void* stream) {
   moe_status st = check_config(cfg);
   if (st != MOE_OK) return st;
-  if (!rt || !rt->perm || !x || !xd) return MOE_ERR_INVALID_ARG;
-  const int R = cfg->T * cfg->k;
-  if (launch_dispatch(rt->perm, x, xd, R, cfg->H, cfg->k, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (!rt || !rt->pos || !x || !xd) return MOE_ERR_INVALID_ARG;
+  if (launch_dispatch(rt->pos, x, xd, cfg->T, cfg->H, cfg->k, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -188,6 +193,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t
   g.yd = yd;
   g.hdr = at<int32_t>(ws, L.header);
   g.tasks = at<int32_t>(ws, L.tasks);
+  g.ngroups = 1;  // the launcher picks the group count from the grid it launches
   g.mb_expert = at<int32_t>(ws, L.mblk_expert);
   g.mb_row0 = at<int32_t>(ws, L.mblk_row0);
   g.mb_rows = at<int32_t>(ws, L.mblk_rows);
@@ -202,7 +208,6 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_forward_reset(g.hdr, g.mb_ready, L.max_mblk, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_gemm(g, L.tile_m, cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }

@@ -14,8 +14,8 @@
 //    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
 //  * The MFMA A operand is the weight tile and the B operand the token tile, so one lane
 //    ends with four consecutive output columns of one token row (8-byte stores).
-//  * Operands are staged through LDS in 64-wide K steps, double buffered, rows swizzled by
-//    XOR of the 16-byte chunk index with the row's low 3 bits (conflict-free 128-bit reads).
+//  * Operands are staged through LDS in 64-wide K steps, double buffered, the 16-byte chunks
+//    of each row XOR-swizzled so that 128-bit fragment reads are free of bank conflicts.
 //  * Every output element accumulates its K products in the same order (ascending K steps of
 //    16 inside one v_mfma_f32_32x32x16_bf16 chain), so tile order, grid size and tile height
 //    never change a result bit.
@@ -45,6 +45,29 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
 
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// LDS swizzle of a 128-byte operand row: its eight 16-byte chunks are permuted by XOR with
+// (row & 7) ^ (bit 3 of row). Any 8 consecutive rows then put one chunk index in 8 distinct
+// 16-byte slots of a 128-byte bank window, and any 16 consecutive rows in 16 distinct slots
+// of a 256-byte window, so a 128-bit fragment read (32 consecutive rows, one chunk) is free of
+// bank conflicts whether the LDS serves 8 or 16 lanes per cycle.
+__device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Scheduling pattern for one k-step region: NM MFMAs with NV global loads, NR LDS reads and
+// NW LDS writes spread evenly between them (each MFMA followed by its share).
+template <int NM, int NV, int NR, int NW, int I = 0>
+struct Interleave {
+  static __device__ __forceinline__ void emit() {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int v = NV * (I + 1) / NM - NV * I / NM;
+    constexpr int r = NR * (I + 1) / NM - NR * I / NM;
+    constexpr int w = NW * (I + 1) / NM - NW * I / NM;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // global loads
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // LDS reads
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);  // LDS writes
+    if constexpr (I + 1 < NM) Interleave<NM, NV, NR, NW, I + 1>::emit();
+  }
+};
+
 template <int BM, int WN, int WM, int MINW>
 __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
@@ -64,7 +87,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
   const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within a 32-row group, chunk
-  const int lds_pchunk = lchunk ^ (lrow & 7);   // swizzled chunk (row & 7 == lrow & 7)
+  const int lds_pchunk = lchunk ^ swz(lrow);    // swizzled chunk (rows 32 apart swizzle alike)
   const int fr_row = lane & 31, fr_chunk = lane >> 5;
 
   const uint32_t yd_bytes = (uint32_t)((size_t)p.R * p.H * 2);
@@ -72,11 +95,33 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
   const __amdgpu_buffer_rsrc_t r_yd = make_rsrc(p.yd, yd_bytes);
   const __amdgpu_buffer_rsrc_t r_act = make_rsrc(p.act, act_bytes);
 
+  // tile source: one shared cursor over the list, or (with kGroups groups) this workgroup's
+  // group takes list chunks g, g + G, g + 2G, ... in order, then those of the other groups in
+  // turn. Each group walks the list in order, so every tile a Linear-2 tile waits for is taken
+  // before it by a workgroup that never waits on a later tile.
+  const int my_group = (int)(blockIdx.x % (unsigned)p.ngroups);
+  const int chunk = max(1, (int)gridDim.x / p.ngroups);  // list positions per chunk
+  int scan_group = 0;  // thread 0 only: groups visited so far
   for (;;) {
     if (tid == 0) {
-      const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
+      int task = kNoTask;
       const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
-      s_task = t < ntasks ? p.tasks[t] : kNoTask;
+      if (p.ngroups == 1) {
+        const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
+        if (t < ntasks) task = p.tasks[t];
+      } else {
+        while (scan_group < p.ngroups) {
+          const int g = (my_group + scan_group) % p.ngroups;
+          const int i = atomicAdd(&p.hdr[HDR_GROUP_CURSOR + g], 1);
+          const long long at = ((long long)(i / chunk) * p.ngroups + g) * chunk + i % chunk;
+          if (at < ntasks) {
+            task = p.tasks[at];
+            break;
+          }
+          ++scan_group;
+        }
+      }
+      s_task = task;
     }
     __syncthreads();
     // the task and its m-block record are the same for the whole workgroup: keep them scalar
@@ -153,51 +198,78 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
         wrow[f] = (f < FN / 2) ? wn * (BN / 2 / WN) + f * 32 : BN / 2 + wn * (BN / 2 / WN) + (f - FN / 2) * 32;
     }
 
+    // Mainloop, software-pipelined by hand. Per K step of 64 (four MFMA k-steps of 16):
+    //   k-step 0 MFMAs | the next K step's global loads + fragments of k-step 1
+    //   k-step 1 MFMAs | fragments of k-step 2
+    //   k-step 2 MFMAs | fragments of k-step 3
+    //   k-step 3 MFMAs | the next K step written into the other LDS stage
+    //   barrier, then fragments of the next K step's k-step 0
+    // Fragments alternate between two register sets so that reads for k-step s + 1 are in
+    // flight while the MFMAs of k-step s run; the sched_group_barrier patterns keep the
+    // compiler from sinking the reads next to their first use.
     u32x4 stage_regs[LD];
-    auto load_k = [&](int kt) {
+    bf16x8 fa[2][FN], fb[2][FM];
+    const int KT = K / BK;
+    auto issue_loads = [&](int kt) {
 #pragma unroll
-      for (int i = 0; i < LD; ++i) {
+      for (int i = 0; i < LD; ++i)
         stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(i < BN / 32 ? r_w : r_t, (int)(i < BN / 32 ? vbase_w : vbase_t),
                                                               (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
-      }
     };
-    auto store_lds = [&](int st) {
+    auto write_lds = [&](int st) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) {
         const int r = lrow + 32 * i;
         *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[i];
       }
     };
-    auto compute = [&](int st) {
+    auto read_frags = [&](int st, int ks, int set) {
       const uint16_t* base = &lds[st * STAGE];
+      const int pc = ((2 * ks + fr_chunk) ^ swz(fr_row)) * 8;
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        const int pc = ((2 * ks + fr_chunk) ^ (fr_row & 7)) * 8;
-        bf16x8 af[FN], bfr[FM];
+      for (int f = 0; f < FN; ++f) fa[set][f] = *reinterpret_cast<const bf16x8*>(base + (wrow[f] + fr_row) * BK + pc);
 #pragma unroll
-        for (int f = 0; f < FN; ++f)
-          af[f] = *reinterpret_cast<const bf16x8*>(base + (wrow[f] + fr_row) * BK + pc);
+      for (int m = 0; m < FM; ++m)
+        fb[set][m] = *reinterpret_cast<const bf16x8*>(base + (BN + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
+    };
+    auto mfmas = [&](int set) {
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
 #pragma unroll
         for (int m = 0; m < FM; ++m)
-          bfr[m] = *reinterpret_cast<const bf16x8*>(base + (BN + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
-#pragma unroll
-        for (int f = 0; f < FN; ++f)
-#pragma unroll
-          for (int m = 0; m < FM; ++m)
-            acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[f], bfr[m], acc[f][m], 0, 0, 0);
-      }
+          acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][f], fb[set][m], acc[f][m], 0, 0, 0);
     };
 
-    const int KT = K / BK;
-    load_k(0);
-    store_lds(0);
+    issue_loads(0);
+    write_lds(0);
     __syncthreads();
+    read_frags(0, 0, 0);
     for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) load_k(kt + 1);
-      compute(kt & 1);
-      if (kt + 1 < KT) store_lds((kt + 1) & 1);
+      const int st = kt & 1;
+      // the last K step reloads itself instead of reading past the operands (never used)
+      const int kn = kt + 1 < KT ? kt + 1 : kt;
+      __builtin_amdgcn_sched_barrier(0);
+      issue_loads(kn);
+      read_frags(st, 1, 1);
+      mfmas(0);
+      Interleave<FN * FM, LD, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, 2, 0);
+      mfmas(1);
+      Interleave<FN * FM, 0, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, 3, 1);
+      mfmas(0);
+      Interleave<FN * FM, 0, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      write_lds(st ^ 1);
+      mfmas(1);
+      Interleave<FN * FM, 0, 0, LD>::emit();
+      __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+      read_frags(st ^ 1, 0, 0);
     }
+    __syncthreads();  // the epilogue's next task reuses both stages
 
     // epilogue: lane holds, for output block (f, m), rows 8g + 4*(lane>>5) + {0..3} of the
     // weight fragment (output columns) at token column lane & 31
@@ -247,23 +319,43 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
     }
     __syncthreads();
   }
+
+  // the last workgroup to leave resets the cursor and the ready counters, so the next
+  // moe_forward on this plan starts clean without a separate launch
+  __shared__ int s_last;
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(&p.hdr[HDR_DONE], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (s_last) {
+    const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
+    for (int i = tid; i < n; i += 256) p.mb_ready[i] = 0;
+    if (tid == 0) {
+      p.hdr[HDR_CURSOR] = 0;
+      for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;
+      p.hdr[HDR_DONE] = 0;
+    }
+  }
 }
 
 template <int BM, int WN, int WM, int MINW>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
   auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
-  int grid = num_workgroups;
-  if (grid <= 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return err;
-    err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (err != hipSuccess) return err;
-    err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
-    if (err != hipSuccess) return err;
-    grid = cus * (per_cu > 0 ? per_cu : 1);
-  }
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, a);
+  // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
+  // group has workgroups that can take its sublist's tiles
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+  if (err != hipSuccess) return err;
+  const int capacity = cus * (per_cu > 0 ? per_cu : 1);
+  int grid = num_workgroups > 0 && num_workgroups < capacity ? num_workgroups : capacity;
+  GemmArgs g = a;
+  g.ngroups = grid >= kGroups ? kGroups : 1;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

@@ -19,10 +19,20 @@ enum : int {
   HDR_TILE_M = 4,
   HDR_N1 = 5,
   HDR_N2 = 6,
-  HDR_SLOTS = 16
+  HDR_DONE = 7,    // persistent workgroups that have exited (the last one resets the state)
+  HDR_GROUP_CURSOR = 8,   // [8, 16): tiles each locality group has taken
+  HDR_SLOTS = 32
 };
 
-constexpr int kTokensPerChunk = 64;  // routing histogram granularity (tokens)
+// Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, which is
+// the XCD it runs on (the hardware deals workgroups to the 8 XCDs round-robin). The list is
+// cut into chunks of (workgroups per group) consecutive tiles, dealt round-robin to the
+// groups; since the list is written in blocks of kBlockM m-blocks x kBlockN n-tiles of one
+// expert, the workgroups sharing an XCD's L2 work on tiles that share operand rows.
+constexpr int kGroups = 8;
+constexpr int kBlockM = 4;
+constexpr int kBlockN = 8;
+
 constexpr int kTileN2 = 256;         // Linear-2 tile: Yd columns
 constexpr int kTileN1 = 128;         // Linear-1 tile: A columns (=> 128 gate + 128 up weight rows)
 constexpr int kTileK = 64;           // K step staged through LDS
@@ -55,7 +65,7 @@ struct PlanArgs {
   int32_t* mb_rows;
   int32_t* mb_ready;
   int32_t* tasks;
-  int T, E, k, chunks;
+  int T, E, k, chunks, chunk_tokens;
   int W;         // experts per wave
   int schedule;  // MOE_SCHED_*
   int lead;      // interleave lead (>= 1)
@@ -69,7 +79,8 @@ struct GemmArgs {
   uint16_t* act;
   uint16_t* yd;
   int32_t* hdr;
-  const int32_t* tasks;
+  const int32_t* tasks;  // the tile list in schedule order
+  int ngroups;           // 1: one shared cursor; kGroups: round-robin chunks per group
   const int32_t* mb_expert;
   const int32_t* mb_row0;
   const int32_t* mb_rows;
@@ -86,11 +97,10 @@ struct GemmArgs {
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s);
 hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s);
 hipError_t launch_scatter(const PlanArgs& a, hipStream_t s);
-hipError_t launch_dispatch(const int32_t* perm, const uint16_t* x, uint16_t* xd, int R, int H, int k,
+hipError_t launch_dispatch(const int32_t* pos, const uint16_t* x, uint16_t* xd, int T, int H, int k,
                            hipStream_t s);
 hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
                           int H, int k, hipStream_t s);
-hipError_t launch_forward_reset(int32_t* hdr, int32_t* mb_ready, int max_mblk, hipStream_t s);
 // Persistent grouped GEMM; grid = num_workgroups (0 = CUs x occupancy).
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s);
 

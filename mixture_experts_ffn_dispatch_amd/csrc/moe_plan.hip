@@ -4,14 +4,16 @@
 // expert (X-Stage paper, Introduction, MoE-layer paragraph); the expert-wave paragraph and
 // Section 4.2 (MegaMoE) fix the tile orders that the schedule builder writes.
 //
-//   route_hist     one wavefront per token: top-k over the E logits (descending, ties to the
-//                  lower expert id), renormalised softmax weights, and a per-(expert, chunk)
-//                  count of the routed slots (LDS atomics on integers: order-free, exact).
+//   route_hist     one block per token chunk, one wavefront per token: top-k over the E
+//                  logits (descending, ties to the lower expert id), renormalised softmax
+//                  weights, and a per-(expert, chunk) count of the routed slots (LDS atomics
+//                  on integers: order-free, exact).
 //   scan_schedule  one workgroup: exclusive scan of the expert-major count table, which gives
 //                  every (expert, chunk) its first dispatched row, the expert offsets, the
 //                  m-block table, zeroed dependency counters and the tile list.
-//   scatter        one wavefront per chunk: stable ranks of the chunk's slots inside their
-//                  expert (ballot/match over 64 slots at a time), perm and pos.
+//   scatter        one block per chunk, its slots split into 16 consecutive runs, one per
+//                  wavefront: per-run expert counts, a per-expert prefix over the runs, then
+//                  stable ranks (ballot/match over 64 slots at a time) give perm and pos.
 #include <math.h>
 
 #include "moe_internal.h"
@@ -24,16 +26,19 @@ __device__ inline bool ranks_before(float av, int ae, float bv, int be) {
   return av > bv || (av == bv && ae < be);
 }
 
+constexpr int kPlanThreads = 1024;  // 16 wavefronts per block in route_hist and scatter
+constexpr int kPlanWaves = kPlanThreads / 64;
+
 template <int R>  // logits held per lane: experts lane, lane + 64, ..., E <= 64 * R
-__global__ __launch_bounds__(256) void route_hist_kernel(PlanArgs a) {
+__global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
   __shared__ int cnt[MOE_MAX_EXPERTS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int chunk = blockIdx.x;
-  for (int e = tid; e < a.E; e += 256) cnt[e] = 0;
+  for (int e = tid; e < a.E; e += kPlanThreads) cnt[e] = 0;
   __syncthreads();
 
-  const int t_end = min(a.T, (chunk + 1) * kTokensPerChunk);
-  for (int t = chunk * kTokensPerChunk + wave; t < t_end; t += 4) {
+  const int t_end = min(a.T, (chunk + 1) * a.chunk_tokens);
+  for (int t = chunk * a.chunk_tokens + wave; t < t_end; t += kPlanWaves) {
     const float* row = a.logits + (size_t)t * a.E;
     float v[R];
 #pragma unroll
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(256) void route_hist_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += 256) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
+  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
 }
 
 constexpr int kScanThreads = 1024;
@@ -215,26 +220,38 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   }
   __syncthreads();
 
-  // 4. write the tile list; within a run tiles go (expert, m-block, n-tile)
-  for (int w = 0; w < nw; ++w) {
-    const int mbw0 = s_mb[w * W];
-    const int a_w = s_a[w], b_w = s_b[w];
-    // Linear-1 tiles of wave w
-    const int b_seg = (interleaved && w >= D) ? s_b[w - D] : -1;  // L2 run it is spread over
-    for (int q = tid; q < a_w; q += kScanThreads) {
-      long long at = s_l1s[w] + q;
-      if (b_seg > 0) {
-        // emitted right after L2 tile number ceil((q+1) * b / a) of its segment
-        at += ((long long)(q + 1) * b_seg + a_w - 1) / a_w;
+  // 4. write the tile list. Inside a run (one wave's Linear-1 or Linear-2 tiles) the tiles of
+  //    each expert are cut into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted
+  //    block by block (m-block major inside a block), so consecutive list positions share
+  //    operand rows. Every tile of a phase is placed independently: tile u of the phase is
+  //    (m-block u / n, n-tile u % n); its expert is found by binary search over s_mb.
+  for (int ph = 0; ph < 2; ++ph) {
+    const int n = ph ? a.n2 : a.n1;
+    for (int u = tid; u < total_mb * n; u += kScanThreads) {
+      const int mb = u / n, nt = u % n;
+      int lo = 0, hi = E - 1;  // expert e with s_mb[e] <= mb < s_mb[e + 1]
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_mb[mid] <= mb) lo = mid;
+        else hi = mid - 1;
       }
-      a.tasks[at] = make_task(0, mbw0 + q / a.n1, q % a.n1);
-    }
-    // Linear-2 tiles of wave w
-    const int a_seg = (interleaved && w + D < nw) ? s_a[w + D] : 0;  // L1 tiles spread over it
-    for (int j = tid; j < b_w; j += kScanThreads) {
-      long long at = s_l2s[w] + j;
-      if (a_seg > 0) at += (long long)j * a_seg / b_w;  // L1 tiles emitted before L2 tile j
-      a.tasks[at] = make_task(1, mbw0 + j / a.n2, j % a.n2);
+      const int e = lo, w = e / W;
+      const int nmb = s_mb[e + 1] - s_mb[e], ml = mb - s_mb[e];
+      const int mg = ml / kBlockM, ng = nt / kBlockN;
+      const int bm_act = min(kBlockM, nmb - mg * kBlockM), bn_act = min(kBlockN, n - ng * kBlockN);
+      const int q = (s_mb[e] - s_mb[w * W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
+                    (ml - mg * kBlockM) * bn_act + (nt - ng * kBlockN);
+      const int run_len = ph ? s_b[w] : s_a[w];
+      // the run it is merged with in the interleaved order (see the position formulas)
+      const int other = !interleaved ? -1 : (ph ? (w + D < nw ? s_a[w + D] : 0) : (w >= D ? s_b[w - D] : -1));
+      long long at = (ph ? s_l2s[w] : s_l1s[w]) + q;
+      if (ph == 0 && other > 0) {
+        // Linear-1 tile q is emitted right after Linear-2 tile ceil((q+1) * b / a) of its segment
+        at += ((long long)(q + 1) * other + run_len - 1) / run_len;
+      } else if (ph == 1 && other > 0) {
+        at += (long long)q * other / run_len;  // Linear-1 tiles emitted before Linear-2 tile q
+      }
+      a.tasks[at] = make_task(ph, mb, nt);
     }
   }
   if (tid == 0) {
@@ -245,21 +262,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_TILE_M] = BM;
     a.hdr[HDR_N1] = a.n1;
     a.hdr[HDR_N2] = a.n2;
+    a.hdr[HDR_DONE] = 0;
+    for (int g = 0; g < kGroups; ++g) a.hdr[HDR_GROUP_CURSOR + g] = 0;
   }
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(PlanArgs a) {
-  __shared__ int run[MOE_MAX_EXPERTS];
-  const int lane = threadIdx.x, chunk = blockIdx.x;
-  for (int e = lane; e < a.E; e += 64) run[e] = a.chunk_counts[(size_t)e * a.chunks + chunk];
-  __syncthreads();
+// Stable ranks of a run of slots inside their experts, 64 slots per step: lanes holding the
+// same expert are found with a ballot, ranked by lane order, and the run's running count
+// `run[e]` (LDS) advances by their number. With `emit`, rows are written out.
+template <bool emit>
+__device__ void rank_run(const PlanArgs& a, int f0, int f1, int* run) {
+  const int lane = threadIdx.x & 63;
   const int R = a.T * a.k;
-  const int f0 = chunk * kTokensPerChunk * a.k;
-  const int f1 = min(R, f0 + kTokensPerChunk * a.k);
   for (int s = f0; s < f1; s += 64) {
     const int f = s + lane;
-    const bool valid = f < f1;
-    int e = valid ? a.topk_ids[f] : -1;
+    int e = f < f1 ? a.topk_ids[f] : -1;
     if ((unsigned)e >= (unsigned)a.E) e = -1;
     unsigned long long remaining = __ballot(e >= 0);
     int row = -1;
@@ -272,25 +289,63 @@ __global__ __launch_bounds__(64) void scatter_kernel(PlanArgs a) {
       if (lane == leader) run[ev] = base + __popcll(m);
       remaining &= ~m;
     }
-    if (e >= 0 && (unsigned)row < (unsigned)R) {
+    if (emit && e >= 0 && (unsigned)row < (unsigned)R) {
       a.perm[row] = f;
       a.pos[f] = row;
     }
   }
 }
 
+__global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
+  // per-wavefront running counts: first the wave's own counts, then its first rows
+  __shared__ int run[kPlanWaves][MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x, wave = tid >> 6, chunk = blockIdx.x;
+  const int R = a.T * a.k;
+  const int c0 = chunk * a.chunk_tokens * a.k;
+  const int c1 = min(R, c0 + a.chunk_tokens * a.k);
+  const int per_wave = ((c1 - c0 + kPlanWaves - 1) / kPlanWaves + 63) / 64 * 64;
+  const int f0 = min(c1, c0 + wave * per_wave), f1 = min(c1, f0 + per_wave);
+  for (int e = tid; e < a.E; e += kPlanThreads)
+    for (int w = 0; w < kPlanWaves; ++w) run[w][e] = 0;
+  __syncthreads();
+  rank_run<false>(a, f0, f1, run[wave]);  // counts of this wave's slots per expert
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kPlanThreads) {
+    int r = a.chunk_counts[(size_t)e * a.chunks + chunk];  // chunk's first row of expert e
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int c = run[w][e];
+      run[w][e] = r;
+      r += c;
+    }
+  }
+  __syncthreads();
+  rank_run<true>(a, f0, f1, run[wave]);
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* perm, const uint16_t* x,
-                                                       uint16_t* xd, int R, int H, int k, int T) {
+// Dispatch, token-major: a wavefront reads token t's row once and writes it to the k
+// dispatched rows pos[t*k + j] (the same bytes as gathering xd[r] = x[perm[r] / k]).
+__global__ __launch_bounds__(256) void dispatch_kernel(const int32_t* pos, const uint16_t* x, uint16_t* xd,
+                                                       int T, int H, int k) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cpr = H / 8;  // 16-byte chunks per row
-  for (int r = blockIdx.x * 4 + wave; r < R; r += gridDim.x * 4) {
-    const int t = perm[r] / k;
-    if ((unsigned)t >= (unsigned)T) continue;
+  const int R = T * k;
+  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * H);
-    u32x4* dst = reinterpret_cast<u32x4*>(xd + (size_t)r * H);
-    for (int c = lane; c < cpr; c += 64) dst[c] = src[c];
+    const int32_t* pt = pos + (size_t)t * k;
+    for (int c = lane; c < cpr; c += 128) {
+      const bool two = c + 64 < cpr;
+      const u32x4 v0 = src[c];
+      const u32x4 v1 = two ? src[c + 64] : v0;
+      for (int j = 0; j < k; ++j) {
+        const int r = pt[j];
+        if ((unsigned)r >= (unsigned)R) continue;
+        u32x4* dst = reinterpret_cast<u32x4*>(xd + (size_t)r * H);
+        dst[c] = v0;
+        if (two) dst[c + 64] = v1;
+      }
+    }
   }
 }
 
@@ -314,10 +369,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const 
       float acc[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
       for (int j = 0; j < k; ++j) {  // fixed ascending order
-        const int r = pt[j];
-        if ((unsigned)r >= (unsigned)R) continue;
-        const float wj = wt[j];
+        int r = pt[j];
+        float wj = wt[j];
+        if ((unsigned)r >= (unsigned)R) {  // never for a plan written by moe_plan
+          r = 0;
+          wj = 0.f;
+        }
         const u32x4 v = reinterpret_cast<const u32x4*>(yd + (size_t)r * H)[c];
         acc[0] = fmaf(wj, bf16_lo(v.x), acc[0]);
         acc[1] = fmaf(wj, bf16_hi(v.x), acc[1]);
@@ -338,17 +397,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const 
   }
 }
 
-__global__ __launch_bounds__(256) void forward_reset_kernel(int32_t* hdr, int32_t* mb_ready,
-                                                            int max_mblk) {
-  const int n = min(hdr[HDR_NMBLK], max_mblk);
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    mb_ready[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    hdr[HDR_CURSOR] = 0;
-    hdr[HDR_ERROR] = 0;
-  }
-}
-
 inline int grid_rows(long long rows_per_block_units) {
   long long g = rows_per_block_units;
   if (g < 1) g = 1;
@@ -360,7 +408,7 @@ inline int grid_rows(long long rows_per_block_units) {
 
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s) {
   const int R = (a.E + 63) / 64;
-  const dim3 grid(a.chunks), block(256);
+  const dim3 grid(a.chunks), block(kPlanThreads);
   if (R <= 1) hipLaunchKernelGGL(route_hist_kernel<1>, grid, block, 0, s, a);
   else if (R <= 2) hipLaunchKernelGGL(route_hist_kernel<2>, grid, block, 0, s, a);
   else if (R <= 4) hipLaunchKernelGGL(route_hist_kernel<4>, grid, block, 0, s, a);
@@ -375,15 +423,13 @@ hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_scatter(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(scatter_kernel, dim3(a.chunks), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3(a.chunks), dim3(kPlanThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const int32_t* perm, const uint16_t* x, uint16_t* xd, int R, int H, int k,
+hipError_t launch_dispatch(const int32_t* pos, const uint16_t* x, uint16_t* xd, int T, int H, int k,
                            hipStream_t s) {
-  const int T = R / k;
-  hipLaunchKernelGGL(dispatch_kernel, dim3(grid_rows((R + 3) / 4)), dim3(256), 0, s, perm, x, xd, R, H,
-                     k, T);
+  hipLaunchKernelGGL(dispatch_kernel, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, x, xd, T, H, k);
   return hipGetLastError();
 }
 
@@ -391,12 +437,6 @@ hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd
                           int H, int k, hipStream_t s) {
   hipLaunchKernelGGL(combine_kernel, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, w, yd, out, T,
                      H, k, T * k);
-  return hipGetLastError();
-}
-
-hipError_t launch_forward_reset(int32_t* hdr, int32_t* mb_ready, int max_mblk, hipStream_t s) {
-  const int blocks = max(1, min(64, (max_mblk + 255) / 256));
-  hipLaunchKernelGGL(forward_reset_kernel, dim3(blocks), dim3(256), 0, s, hdr, mb_ready, max_mblk);
   return hipGetLastError();
 }
 

@@ -42,7 +42,7 @@ def _cfg(**kw):
 def test_layout_is_consistent():
     L = moe.moe_workspace_layout(_cfg())
     assert L["tile_m"] == 256 and L["n1_tiles"] == 16 and L["n2_tiles"] == 28
-    assert L["chunks"] == 64
+    assert L["chunk_tokens"] == 16 and L["chunks"] == 256
     # max m-blocks: every row of every active expert fills tiles, plus one partial per expert
     assert L["max_mblk"] == (4096 * 8 + 32 * 255) // 256
     assert L["max_tasks"] == L["max_mblk"] * (16 + 28)

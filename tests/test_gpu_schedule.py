@@ -25,8 +25,28 @@ def workload():
     return d, Device(d)
 
 
+BLOCK_M, BLOCK_N = 4, 8  # tiles of one expert emitted together: m-blocks x n-tiles
+
+
+def run_tiles(phase, wave_experts, mb_of, n):
+    """One run's tiles in emission order, with each tile's block number inside the run: per
+    expert, blocks of up to BLOCK_M m-blocks x BLOCK_N n-tiles; m-block major inside a block."""
+    out = []
+    blk = 0
+    for e in wave_experts:
+        mbs = mb_of[e]
+        for m0 in range(0, len(mbs), BLOCK_M):
+            for n0 in range(0, n, BLOCK_N):
+                for mb in mbs[m0:m0 + BLOCK_M]:
+                    for nt in range(n0, min(n, n0 + BLOCK_N)):
+                        out.append(((phase, mb, nt), blk))
+                blk += 1
+    return out, blk
+
+
 def model_order(counts, tile_m, n1, n2, W_, schedule, lead):
-    """Sequential model: walk the waves and emit tiles one at a time."""
+    """Sequential model: walk the waves and emit tiles one at a time. Returns the list of
+    (phase, m-block, n-tile)."""
     E = len(counts)
     mb_of = []  # m-block ids per expert, in expert order
     nxt = 0
@@ -35,34 +55,42 @@ def model_order(counts, tile_m, n1, n2, W_, schedule, lead):
         mb_of.append(list(range(nxt, nxt + nb)))
         nxt += nb
     nw = -(-E // W_)
-    waves = [[mb for e in range(w * W_, min(E, (w + 1) * W_)) for mb in mb_of[e]] for w in range(nw)]
-    L1 = [[(0, mb, n) for mb in wv for n in range(n1)] for wv in waves]
-    L2 = [[(1, mb, n) for mb in wv for n in range(n2)] for wv in waves]
+    L1, L2 = [], []
+    for w in range(nw):
+        experts = range(w * W_, min(E, (w + 1) * W_))
+        for ph, n, dst in ((0, n1, L1), (1, n2, L2)):
+            tiles, _ = run_tiles(ph, experts, mb_of, n)
+            dst.append([t for t, _ in tiles])
     if schedule == moe.MOE_SCHED_EXPERT_WAVE:
-        return [t for w in range(nw) for t in L1[w] + L2[w]]
-    D = max(1, lead)
-    out = [t for w in range(min(D, nw)) for t in L1[w]]
-    for i in range(nw):
-        l2 = L2[i]
-        l1 = L1[i + D] if i + D < nw else []
-        done = 0
-        for j, t in enumerate(l2, 1):
-            out.append(t)
-            target = j * len(l1) // len(l2)
-            while done < target:
-                out.append(l1[done])
-                done += 1
-        out.extend(l1[done:])
-    return out
+        seq = [x for w in range(nw) for x in L1[w] + L2[w]]
+    else:
+        D = max(1, lead)
+        seq = [x for w in range(min(D, nw)) for x in L1[w]]
+        for i in range(nw):
+            l2 = L2[i]
+            l1 = L1[i + D] if i + D < nw else []
+            done = 0
+            for j, t in enumerate(l2, 1):
+                seq.append(t)
+                target = j * len(l1) // len(l2)
+                while done < target:
+                    seq.append(l1[done])
+                    done += 1
+            seq.extend(l1[done:])
+    return seq
+
+
+def decode(raw):
+    raw = raw.astype(np.int64) & 0xFFFFFFFF
+    return [(int(t >> 31), int((t >> 12) & 0x7FFFF), int(t & 0xFFF)) for t in raw]
 
 
 def read_tasks(cfg, bufs):
     L = moe.moe_workspace_layout(cfg)
     ws = bufs["ws"].cpu().numpy()
-    hdr = ws[:64].view(np.int32)
+    hdr = ws[:128].view(np.int32)
     n = int(hdr[2])
-    raw = ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32).astype(np.int64) & 0xFFFFFFFF
-    return [(int(t >> 31), int((t >> 12) & 0x7FFFF), int(t & 0xFFF)) for t in raw], L
+    return decode(ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32)), L
 
 
 @pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9)])
@@ -74,8 +102,8 @@ def test_task_list_matches_model(workload, schedule, lead, tile_m):
     b = run(cfg, dev)
     tasks, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
-    expect = model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], SHAPE.experts_per_wave, schedule, lead)
-    assert tasks == expect
+    assert tasks == model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], SHAPE.experts_per_wave,
+                                schedule, lead)
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
     seen = {}
     for ph, mb, _ in tasks:
