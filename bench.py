@@ -125,6 +125,7 @@ def main() -> int:
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--lib", default=None, help="load this build of libmoe instead of the in-tree one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -143,6 +144,7 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    moe.load(args.lib)
     s = W.shape(args.workload)
     log(f"workload {W.describe(s)}")
     t0 = time.perf_counter()

@@ -80,14 +80,16 @@ class MoeConfig:
 _lib = None
 
 
-def load() -> ctypes.CDLL:
-    """Load libmoe.so (built in-tree by ``mixture_experts_ffn_dispatch_amd.build``)."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree by ``mixture_experts_ffn_dispatch_amd.build``). A different
+    build of the same ABI may be named by ``path`` on the first call."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m mixture_experts_ffn_dispatch_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_ffn_dispatch_amd.build`")
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     vp = ctypes.c_void_p
     sig = {

@@ -54,12 +54,14 @@ __device__ inline int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 // Scheduling pattern for one k-step region: NM MFMAs with NV global loads, NR LDS reads and
 // NW LDS writes spread evenly between them (each MFMA followed by its share).
+// LDS reads go out over the first half of the MFMAs, so they land well before their use.
 template <int NM, int NV, int NR, int NW, int I = 0>
 struct Interleave {
   static __device__ __forceinline__ void emit() {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    constexpr int NMR = NM > 1 ? NM / 2 : 1;
     constexpr int v = NV * (I + 1) / NM - NV * I / NM;
-    constexpr int r = NR * (I + 1) / NM - NR * I / NM;
+    constexpr int r = I < NMR ? NR * (I + 1) / NMR - NR * I / NMR : 0;
     constexpr int w = NW * (I + 1) / NM - NW * I / NM;
     if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // global loads
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // LDS reads
@@ -69,16 +71,18 @@ struct Interleave {
 };
 
 template <int BM, int WN, int WM, int MINW>
-__global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) {
+__global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
   constexpr int FN = BN / WN / 32;  // 32x32 MFMA blocks per wave along weight rows
   constexpr int FM = BM / WM / 32;  // ... along token rows
   constexpr int ROWS = BN + BM;     // LDS rows per stage: weights first, then tokens
   constexpr int STAGE = ROWS * BK;  // bf16 elements per stage
-  constexpr int LD = ROWS / 32;     // 16-byte chunks each thread stages per K step
+  constexpr int NT = 64 * WN * WM;  // threads
+  constexpr int RG = NT / 8;        // operand rows staged per thread-wide step (8 chunks a row)
+  constexpr int LD = ROWS / RG;     // 16-byte chunks each thread stages per K step
   static_assert(FN % 2 == 0 && FN >= 2 && FM >= 1, "tile shape");
-  static_assert(WN * WM == 4, "four wavefronts");
+  static_assert(BM % RG == 0 && BN % (2 * RG) == 0 && RG % 16 == 0, "staging groups");
   static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
@@ -86,8 +90,8 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
-  const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within a 32-row group, chunk
-  const int lds_pchunk = lchunk ^ swz(lrow);    // swizzled chunk (rows 32 apart swizzle alike)
+  const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, chunk
+  const int lds_pchunk = lchunk ^ swz(lrow);    // swizzled chunk (rows RG apart swizzle alike)
   const int fr_row = lane & 31, fr_chunk = lane >> 5;
 
   const uint32_t yd_bytes = (uint32_t)((size_t)p.R * p.H * 2);
@@ -174,11 +178,11 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
     const uint32_t vbase_t = (uint32_t)lrow * rowb + (uint32_t)lchunk * 16u;
     const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
     auto chunk_soff = [&](int i) -> uint32_t {
-      if (i < BN / 32) {
-        if (l2) return (uint32_t)i * 32u * rowb;
-        return i < BN / 64 ? (uint32_t)i * 32u * rowb : up_off + (uint32_t)(i - BN / 64) * 32u * rowb;
+      if (i < BN / RG) {
+        if (l2) return (uint32_t)i * RG * rowb;
+        return i < BN / (2 * RG) ? (uint32_t)i * RG * rowb : up_off + (uint32_t)(i - BN / (2 * RG)) * RG * rowb;
       }
-      return (uint32_t)(i - BN / 32) * 32u * rowb;
+      return (uint32_t)(i - BN / RG) * RG * rowb;
     };
 
     f32x16 acc[FN][FM];
@@ -213,13 +217,13 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
     auto issue_loads = [&](int kt) {
 #pragma unroll
       for (int i = 0; i < LD; ++i)
-        stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(i < BN / 32 ? r_w : r_t, (int)(i < BN / 32 ? vbase_w : vbase_t),
+        stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(i < BN / RG ? r_w : r_t, (int)(i < BN / RG ? vbase_w : vbase_t),
                                                               (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
     };
     auto write_lds = [&](int st) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) {
-        const int r = lrow + 32 * i;
+        const int r = lrow + RG * i;
         *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[i];
       }
     };
@@ -330,7 +334,7 @@ __global__ __launch_bounds__(256, MINW) void gemm_persistent_kernel(GemmArgs p) 
   __syncthreads();
   if (s_last) {
     const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
-    for (int i = tid; i < n; i += 256) p.mb_ready[i] = 0;
+    for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
     if (tid == 0) {
       p.hdr[HDR_CURSOR] = 0;
       for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;
@@ -349,13 +353,14 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
   if (err != hipSuccess) return err;
   err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (err != hipSuccess) return err;
-  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, 0);
+  constexpr int NT = 64 * WN * WM;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NT, 0);
   if (err != hipSuccess) return err;
   const int capacity = cus * (per_cu > 0 ? per_cu : 1);
   int grid = num_workgroups > 0 && num_workgroups < capacity ? num_workgroups : capacity;
   GemmArgs g = a;
   g.ngroups = grid >= kGroups ? kGroups : 1;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -363,7 +368,7 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
   switch (tile_m) {
-    case 256: return launch_variant<256, 2, 2, 1>(a, num_workgroups, s);
+    case 256: return launch_variant<256, 2, 4, 2>(a, num_workgroups, s);
     case 128: return launch_variant<128, 2, 2, 1>(a, num_workgroups, s);
     case 64: return launch_variant<64, 4, 1, 2>(a, num_workgroups, s);
     case 32: return launch_variant<32, 4, 1, 2>(a, num_workgroups, s);
