@@ -107,7 +107,8 @@ typedef struct moe_ws_layout {
   size_t header;        /* int32[32]: [0] error code, [1] task cursor, [2] task count,
                            [3] m-block count, [4] tile_m, [5] L1 n-tiles per m-block,
                            [6] L2 n-tiles per m-block, [7] exited workgroups,
-                           [8..15] tiles taken by each locality group              */
+                           [8..15] units finished by each locality group,
+                           [16] units in the unit table                             */
   size_t chunk_counts;  /* int32[E * chunks]: per-(expert, token chunk) counts, then bases */
   size_t mblk_expert;   /* int32[max_mblk]                                        */
   size_t mblk_row0;     /* int32[max_mblk]                                        */
@@ -115,6 +116,10 @@ typedef struct moe_ws_layout {
   size_t mblk_ready;    /* int32[max_mblk]: Linear-1 tiles finished per m-block   */
   size_t tasks;         /* int32[max_tasks]: the tile list in schedule order; bit 31 = Linear-2,
                            bits 30..12 m-block, bits 11..0 n-tile                    */
+  size_t unit_start;    /* int32[max_tasks + 1]: list position of each unit's first tile
+                           (a unit: up to 32 consecutive tiles of one wave's Linear-1 or
+                           Linear-2 run; header[16] holds the unit count)           */
+  size_t unit_taken;    /* int32[max_tasks]: tiles taken from each unit by moe_forward */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;

@@ -100,11 +100,11 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   const __amdgpu_buffer_rsrc_t r_act = make_rsrc(p.act, act_bytes);
 
   // tile source: one shared cursor over the list, or (with kGroups groups) this workgroup's
-  // group takes list chunks g, g + G, g + 2G, ... in order, then those of the other groups in
-  // turn. Each group walks the list in order, so every tile a Linear-2 tile waits for is taken
-  // before it by a workgroup that never waits on a later tile.
+  // group takes its units g, g + G, g + 2G, ... one after the other, each unit's tiles in
+  // order, then the other groups' units in turn. Each group walks the list in order, so every
+  // tile a Linear-2 tile waits for is taken before it by a workgroup that never waits on a
+  // later tile.
   const int my_group = (int)(blockIdx.x % (unsigned)p.ngroups);
-  const int chunk = max(1, (int)gridDim.x / p.ngroups);  // list positions per chunk
   int scan_group = 0;  // thread 0 only: groups visited so far
   for (;;) {
     if (tid == 0) {
@@ -114,15 +114,22 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
         if (t < ntasks) task = p.tasks[t];
       } else {
+        const int nunits = min(p.hdr[HDR_NUNITS], p.max_units);
         while (scan_group < p.ngroups) {
           const int g = (my_group + scan_group) % p.ngroups;
-          const int i = atomicAdd(&p.hdr[HDR_GROUP_CURSOR + g], 1);
-          const long long at = ((long long)(i / chunk) * p.ngroups + g) * chunk + i % chunk;
-          if (at < ntasks) {
-            task = p.tasks[at];
+          const int j = __hip_atomic_load(&p.hdr[HDR_GROUP_CURSOR + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int u = g + p.ngroups * j;
+          if (u >= nunits) {
+            ++scan_group;
+            continue;
+          }
+          const int lo = p.unit_start[u], hi = min(p.unit_start[u + 1], ntasks);
+          const int t = atomicAdd(&p.unit_taken[u], 1);
+          if (lo + t < hi) {
+            task = p.tasks[lo + t];
             break;
           }
-          ++scan_group;
+          atomicCAS(&p.hdr[HDR_GROUP_CURSOR + g], j, j + 1);  // unit used up: move the group on
         }
       }
       s_task = task;
@@ -335,6 +342,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   if (s_last) {
     const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
     for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
+    const int nu = min(p.hdr[HDR_NUNITS], p.max_units);
+    for (int i = tid; i < nu; i += NT) p.unit_taken[i] = 0;
     if (tid == 0) {
       p.hdr[HDR_CURSOR] = 0;
       for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;

@@ -20,16 +20,18 @@ enum : int {
   HDR_N1 = 5,
   HDR_N2 = 6,
   HDR_DONE = 7,    // persistent workgroups that have exited (the last one resets the state)
-  HDR_GROUP_CURSOR = 8,   // [8, 16): tiles each locality group has taken
+  HDR_GROUP_CURSOR = 8,   // [8, 16): units each locality group has finished
+  HDR_NUNITS = 16,        // units in the unit table
   HDR_SLOTS = 32
 };
 
 // Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, which is
 // the XCD it runs on (the hardware deals workgroups to the 8 XCDs round-robin). The list is
-// cut into chunks of (workgroups per group) consecutive tiles, dealt round-robin to the
-// groups; since the list is written in blocks of kBlockM m-blocks x kBlockN n-tiles of one
-// expert, the workgroups sharing an XCD's L2 work on tiles that share operand rows.
+// made of units (kUnit consecutive tiles of one run, written in blocks of kBlockM m-blocks x
+// kBlockN n-tiles of one expert); unit u belongs to group u % kGroups, so the workgroups that
+// share an XCD's L2 work on tiles of one unit, which share operand rows.
 constexpr int kGroups = 8;
+constexpr int kUnit = 32;
 constexpr int kBlockM = 4;
 constexpr int kBlockN = 8;
 
@@ -65,6 +67,9 @@ struct PlanArgs {
   int32_t* mb_rows;
   int32_t* mb_ready;
   int32_t* tasks;
+  int32_t* unit_start;  // [max_units + 1]: list position of each unit's first tile
+  int32_t* unit_taken;  // [max_units]: tiles taken from each unit in the current forward
+  int max_units;
   int T, E, k, chunks, chunk_tokens;
   int W;         // experts per wave
   int schedule;  // MOE_SCHED_*
@@ -80,7 +85,10 @@ struct GemmArgs {
   uint16_t* yd;
   int32_t* hdr;
   const int32_t* tasks;  // the tile list in schedule order
-  int ngroups;           // 1: one shared cursor; kGroups: round-robin chunks per group
+  const int32_t* unit_start;
+  int32_t* unit_taken;
+  int max_units;
+  int ngroups;  // 1: one shared cursor over the list; kGroups: each group takes its own units
   const int32_t* mb_expert;
   const int32_t* mb_row0;
   const int32_t* mb_rows;

@@ -96,6 +96,8 @@ __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
 
 constexpr int kScanThreads = 1024;
 
+__device__ inline int units_of(int tiles) { return (tiles + kUnit - 1) / kUnit; }
+
 // Exclusive scan of one int per thread over a 1024-thread workgroup; `total` gets the sum.
 __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -129,6 +131,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   __shared__ int s_mb[MOE_MAX_EXPERTS + 1];   // first m-block of each expert
   __shared__ int s_l1s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-1 run
   __shared__ int s_l2s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-2 run
+  __shared__ int s_l1u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-1 unit
+  __shared__ int s_l2u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-2 unit
   __shared__ int s_a[MOE_MAX_EXPERTS];        // Linear-1 tiles per wave
   __shared__ int s_b[MOE_MAX_EXPERTS];        // Linear-2 tiles per wave
   const int tid = threadIdx.x;
@@ -184,9 +188,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     }
   }
   for (int i = tid; i < total_mb; i += kScanThreads) a.mb_ready[i] = 0;
+  for (int i = tid; i < a.max_units; i += kScanThreads) a.unit_taken[i] = 0;
   __syncthreads();
 
-  // 3. tile counts per expert wave and where each wave's runs start in the list
+  // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
+  //    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
+  //    last unit may be shorter); the orders are defined on units, so every unit is one
+  //    contiguous stretch of the list holding tiles of a single run.
   const int W = a.W, nw = (E + W - 1) / W, D = a.lead;
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
   int aw = 0, bw = 0;
@@ -198,33 +206,53 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     s_b[tid] = bw;
   }
   __syncthreads();
-  int unused;
+  const int auw = units_of(aw), buw = units_of(bw);
+  int total_units;
   if (!interleaved) {
     // Expert-Wave order: L1(0) L2(0) L1(1) L2(1) ...
+    int unused;
     const int st = block_exclusive_scan(aw + bw, s_tmp, unused);
+    const int su = block_exclusive_scan(auw + buw, s_tmp, total_units);
     if (tid < nw) {
       s_l1s[tid] = st;
       s_l2s[tid] = st + aw;
+      s_l1u[tid] = su;
+      s_l2u[tid] = su + auw;
     }
   } else {
     // interleaved: L1(0) .. L1(D-1), then segment i = L2(i) merged with L1(i + D)
-    int prefix_total;
-    const int p = block_exclusive_scan(tid < min(D, nw) ? aw : 0, s_tmp, prefix_total);
-    const int seg = tid < nw ? bw + (tid + D < nw ? s_a[tid + D] : 0) : 0;
+    int prefix_total, prefix_units, unused, seg_units;
+    const bool lead = tid < min(D, nw);
+    const int p = block_exclusive_scan(lead ? aw : 0, s_tmp, prefix_total);
+    const int pu = block_exclusive_scan(lead ? auw : 0, s_tmp, prefix_units);
+    const int a_next = tid + D < nw ? s_a[tid + D] : 0;
+    const int seg = tid < nw ? bw + a_next : 0;
+    const int segu = tid < nw ? buw + units_of(a_next) : 0;
     const int q = prefix_total + block_exclusive_scan(seg, s_tmp, unused);
+    const int qu = prefix_units + block_exclusive_scan(segu, s_tmp, seg_units);
+    total_units = prefix_units + seg_units;
     if (tid < nw) {
-      s_l2s[tid] = q;                      // segment tid starts with L2(tid)
-      if (tid < D) s_l1s[tid] = p;         // lead prefix
-      if (tid + D < nw) s_l1s[tid + D] = q;  // L1(tid + D) lives in segment tid
+      s_l2s[tid] = q;  // segment tid starts with L2(tid)
+      s_l2u[tid] = qu;
+      if (tid < D) {  // lead prefix
+        s_l1s[tid] = p;
+        s_l1u[tid] = pu;
+      }
+      if (tid + D < nw) {  // L1(tid + D) lives in segment tid
+        s_l1s[tid + D] = q;
+        s_l1u[tid + D] = qu;
+      }
     }
   }
   __syncthreads();
 
-  // 4. write the tile list. Inside a run (one wave's Linear-1 or Linear-2 tiles) the tiles of
-  //    each expert are cut into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted
-  //    block by block (m-block major inside a block), so consecutive list positions share
-  //    operand rows. Every tile of a phase is placed independently: tile u of the phase is
-  //    (m-block u / n, n-tile u % n); its expert is found by binary search over s_mb.
+  // 4. write the tile list and the unit table. Inside a run the tiles of each expert are cut
+  //    into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted block by block
+  //    (m-block major inside a block), so neighbouring positions share operand rows. Every
+  //    tile of a phase is placed independently: tile u of the phase is (m-block u / n, n-tile
+  //    u % n); its expert is found by binary search over s_mb. In a merged segment, Linear-1
+  //    unit v goes right after Linear-2 unit ceil((v+1) * bu / au) (bu, au: unit counts), which
+  //    spreads the Linear-1 units evenly and ends the segment with the last Linear-1 unit.
   for (int ph = 0; ph < 2; ++ph) {
     const int n = ph ? a.n2 : a.n1;
     for (int u = tid; u < total_mb * n; u += kScanThreads) {
@@ -241,19 +269,29 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       const int bm_act = min(kBlockM, nmb - mg * kBlockM), bn_act = min(kBlockN, n - ng * kBlockN);
       const int q = (s_mb[e] - s_mb[w * W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
                     (ml - mg * kBlockM) * bn_act + (nt - ng * kBlockN);
-      const int run_len = ph ? s_b[w] : s_a[w];
-      // the run it is merged with in the interleaved order (see the position formulas)
-      const int other = !interleaved ? -1 : (ph ? (w + D < nw ? s_a[w + D] : 0) : (w >= D ? s_b[w - D] : -1));
-      long long at = (ph ? s_l2s[w] : s_l1s[w]) + q;
-      if (ph == 0 && other > 0) {
-        // Linear-1 tile q is emitted right after Linear-2 tile ceil((q+1) * b / a) of its segment
-        at += ((long long)(q + 1) * other + run_len - 1) / run_len;
-      } else if (ph == 1 && other > 0) {
-        at += (long long)q * other / run_len;  // Linear-1 tiles emitted before Linear-2 tile q
+      const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
+      long long at;
+      int unit;
+      if (!interleaved || (ph == 0 && w < D)) {
+        at = (long long)(ph ? s_l2s[w] : s_l1s[w]) + q;
+        unit = (ph ? s_l2u[w] : s_l1u[w]) + ur;
+      } else if (ph == 1) {  // Linear-2 unit ur of segment w
+        const int bu = units_of(s_b[w]);
+        const int au = w + D < nw ? units_of(s_a[w + D]) : 0;
+        const int l1_before = au ? (int)((long long)ur * au / bu) : 0;  // all full units
+        at = (long long)s_l2s[w] + (long long)(ur + l1_before) * kUnit + o;
+        unit = s_l2u[w] + ur + l1_before;
+      } else {  // Linear-1 unit ur of wave w, in segment w - D
+        const int b = s_b[w - D], bu = units_of(b), au = units_of(s_a[w]);
+        const int c = bu ? (int)(((long long)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
+        at = (long long)s_l1s[w] + (long long)ur * kUnit + (c == bu ? b : c * kUnit) + o;
+        unit = s_l1u[w] + ur + c;
       }
       a.tasks[at] = make_task(ph, mb, nt);
+      if (o == 0) a.unit_start[unit] = (int)at;
     }
   }
+  if (tid == 0) a.unit_start[total_units] = total_mb * (a.n1 + a.n2);
   if (tid == 0) {
     a.hdr[HDR_ERROR] = 0;
     a.hdr[HDR_CURSOR] = 0;
@@ -263,6 +301,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_N1] = a.n1;
     a.hdr[HDR_N2] = a.n2;
     a.hdr[HDR_DONE] = 0;
+    a.hdr[HDR_NUNITS] = total_units;
     for (int g = 0; g < kGroups; ++g) a.hdr[HDR_GROUP_CURSOR + g] = 0;
   }
 }

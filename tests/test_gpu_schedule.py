@@ -25,28 +25,26 @@ def workload():
     return d, Device(d)
 
 
-BLOCK_M, BLOCK_N = 4, 8  # tiles of one expert emitted together: m-blocks x n-tiles
+BLOCK_M, BLOCK_N, UNIT = 4, 8, 32  # tile blocks of one expert; units of consecutive tiles
 
 
 def run_tiles(phase, wave_experts, mb_of, n):
-    """One run's tiles in emission order, with each tile's block number inside the run: per
-    expert, blocks of up to BLOCK_M m-blocks x BLOCK_N n-tiles; m-block major inside a block."""
+    """One run's tiles in emission order: per expert, blocks of up to BLOCK_M m-blocks x
+    BLOCK_N n-tiles, m-block major inside a block."""
     out = []
-    blk = 0
     for e in wave_experts:
         mbs = mb_of[e]
         for m0 in range(0, len(mbs), BLOCK_M):
             for n0 in range(0, n, BLOCK_N):
                 for mb in mbs[m0:m0 + BLOCK_M]:
                     for nt in range(n0, min(n, n0 + BLOCK_N)):
-                        out.append(((phase, mb, nt), blk))
-                blk += 1
-    return out, blk
+                        out.append((phase, mb, nt))
+    return out
 
 
 def model_order(counts, tile_m, n1, n2, W_, schedule, lead):
-    """Sequential model: walk the waves and emit tiles one at a time. Returns the list of
-    (phase, m-block, n-tile)."""
+    """Sequential model: cut every run into units of UNIT tiles and walk the waves, emitting
+    one unit at a time. Returns the units in list order (lists of (phase, m-block, n-tile))."""
     E = len(counts)
     mb_of = []  # m-block ids per expert, in expert order
     nxt = 0
@@ -55,28 +53,27 @@ def model_order(counts, tile_m, n1, n2, W_, schedule, lead):
         mb_of.append(list(range(nxt, nxt + nb)))
         nxt += nb
     nw = -(-E // W_)
-    L1, L2 = [], []
-    for w in range(nw):
-        experts = range(w * W_, min(E, (w + 1) * W_))
-        for ph, n, dst in ((0, n1, L1), (1, n2, L2)):
-            tiles, _ = run_tiles(ph, experts, mb_of, n)
-            dst.append([t for t, _ in tiles])
+
+    def units(run):
+        return [run[i:i + UNIT] for i in range(0, len(run), UNIT)]
+
+    L1 = [units(run_tiles(0, range(w * W_, min(E, (w + 1) * W_)), mb_of, n1)) for w in range(nw)]
+    L2 = [units(run_tiles(1, range(w * W_, min(E, (w + 1) * W_)), mb_of, n2)) for w in range(nw)]
     if schedule == moe.MOE_SCHED_EXPERT_WAVE:
-        seq = [x for w in range(nw) for x in L1[w] + L2[w]]
-    else:
-        D = max(1, lead)
-        seq = [x for w in range(min(D, nw)) for x in L1[w]]
-        for i in range(nw):
-            l2 = L2[i]
-            l1 = L1[i + D] if i + D < nw else []
-            done = 0
-            for j, t in enumerate(l2, 1):
-                seq.append(t)
-                target = j * len(l1) // len(l2)
-                while done < target:
-                    seq.append(l1[done])
-                    done += 1
-            seq.extend(l1[done:])
+        return [u for w in range(nw) for u in L1[w] + L2[w]]
+    D = max(1, lead)
+    seq = [u for w in range(min(D, nw)) for u in L1[w]]
+    for i in range(nw):
+        l2 = L2[i]
+        l1 = L1[i + D] if i + D < nw else []
+        done = 0
+        for j, u in enumerate(l2, 1):
+            seq.append(u)
+            target = j * len(l1) // len(l2)
+            while done < target:
+                seq.append(l1[done])
+                done += 1
+        seq.extend(l1[done:])
     return seq
 
 
@@ -89,21 +86,38 @@ def read_tasks(cfg, bufs):
     L = moe.moe_workspace_layout(cfg)
     ws = bufs["ws"].cpu().numpy()
     hdr = ws[:128].view(np.int32)
-    n = int(hdr[2])
-    return decode(ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32)), L
+    n, nunits = int(hdr[2]), int(hdr[16])
+    tasks = decode(ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32))
+    starts = ws[L["unit_start"]:L["unit_start"] + 4 * (nunits + 1)].view(np.int32).tolist()
+    return tasks, starts, L
+
+
+# long runs: several full units per run, so the unit-level merge is exercised
+LONG = W.shape(T=2048, H=256, I=512, E=8, k=4, experts_per_wave=2, seed=43, x_std=1.0, w_std=0.05)
+
+
+@pytest.fixture(scope="module")
+def long_workload():
+    return Device(W.generate(LONG))
 
 
 @pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9)])
 @pytest.mark.parametrize("tile_m", [32, 128])
-def test_task_list_matches_model(workload, schedule, lead, tile_m):
-    d, dev = workload
-    cfg = make_cfg(SHAPE, schedule=schedule, lead_waves=lead, tile_m=tile_m)
-    note(f"task list schedule={schedule} lead={lead} tile_m={tile_m}")
+@pytest.mark.parametrize("which", ["short", "long"])
+def test_task_list_matches_model(workload, long_workload, which, schedule, lead, tile_m):
+    shape, dev = (SHAPE, workload[1]) if which == "short" else (LONG, long_workload)
+    cfg = make_cfg(shape, schedule=schedule, lead_waves=lead, tile_m=tile_m)
+    note(f"task list {which} schedule={schedule} lead={lead} tile_m={tile_m}")
     b = run(cfg, dev)
-    tasks, L = read_tasks(cfg, b)
+    tasks, starts, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
-    assert tasks == model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], SHAPE.experts_per_wave,
-                                schedule, lead)
+    units = model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], shape.experts_per_wave, schedule, lead)
+    assert tasks == [t for u in units for t in u]
+    # the unit table marks where each unit starts, the last entry is the list length
+    expect_starts = [0]
+    for u in units:
+        expect_starts.append(expect_starts[-1] + len(u))
+    assert starts == expect_starts
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
     seen = {}
     for ph, mb, _ in tasks:
