@@ -125,15 +125,15 @@ def main() -> int:
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
-    ap.add_argument("--lib", default=None, help="load this build of libmoe instead of the in-tree one")
+    ap.add_argument("--lib", default=None, help="load another build of libmoe (same ABI) instead of the in-tree one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU's share of the layer; runs on more than one GPU are not part "
-            "of this build (expert parallelism across GPUs is described, not built). Use --gpus 1.")
+        log("bench.py measures one GPU's share of the layer and runs on exactly one GPU; the "
+            "expert-parallel exchange across GPUs is not implemented. Use --gpus 1.")
         return 2
 
     import numpy as np
