@@ -3,7 +3,7 @@
 Follows the MoE-layer paragraph of the Introduction of "X-Stage: An Overlooked Pipeline Stage
 for Communication-Computation Overlap in DiT Inference": route -> Dispatch -> Linear-1 ->
 SwiGLU -> Linear-2 -> Combine with the router weights. Steps the page leaves open are fixed
-by these readings (each one is listed with its reason in the design notes):
+by these readings:
 
   routing   softmax over all E router logits, keep the k largest logits (descending; equal
             logits -> lower expert id first), renormalise the kept probabilities to sum to 1;
