@@ -108,7 +108,7 @@ typedef struct moe_ws_layout {
                            [3] m-block count, [4] tile_m, [5] L1 n-tiles per m-block,
                            [6] L2 n-tiles per m-block, [7] exited workgroups,
                            [8..15] units finished by each locality group,
-                           [16] units in the unit table                             */
+                           [16] units in the unit table, [17..25] group unit lists */
   size_t chunk_counts;  /* int32[E * chunks]: per-(expert, token chunk) counts, then bases */
   size_t mblk_expert;   /* int32[max_mblk]                                        */
   size_t mblk_row0;     /* int32[max_mblk]                                        */
@@ -120,6 +120,9 @@ typedef struct moe_ws_layout {
                            (a unit: up to 32 consecutive tiles of one wave's Linear-1 or
                            Linear-2 run; header[16] holds the unit count)           */
   size_t unit_taken;    /* int32[max_tasks]: tiles taken from each unit by moe_forward */
+  size_t group_units;   /* int32[max_tasks]: the units of locality group 0 in list order,
+                           then those of group 1, ... (group g: entries
+                           [header[17+g], header[18+g]))                           */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;

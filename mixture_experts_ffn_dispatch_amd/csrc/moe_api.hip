@@ -87,6 +87,8 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   off = align_up(off + ((size_t)max_tasks + 1) * 4, 256);
   L->unit_taken = off;
   off = align_up(off + (size_t)max_tasks * 4, 256);
+  L->group_units = off;
+  off = align_up(off + (size_t)max_tasks * 4, 256);
   L->total_bytes = off;
   return MOE_OK;
 }
@@ -156,6 +158,7 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.tasks = at<int32_t>(ws, L.tasks);
   a.unit_start = at<int32_t>(ws, L.unit_start);
   a.unit_taken = at<int32_t>(ws, L.unit_taken);
+  a.group_units = at<int32_t>(ws, L.group_units);
   a.max_units = L.max_tasks;
   a.T = cfg->T;
   a.E = cfg->E;
@@ -202,6 +205,7 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t
   g.tasks = at<int32_t>(ws, L.tasks);
   g.unit_start = at<int32_t>(ws, L.unit_start);
   g.unit_taken = at<int32_t>(ws, L.unit_taken);
+  g.group_units = at<int32_t>(ws, L.group_units);
   g.max_units = L.max_tasks;
   g.ngroups = 1;  // the launcher picks the group count from the grid it launches
   g.mb_expert = at<int32_t>(ws, L.mblk_expert);

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  __shared__ int s_task;
+  // The task word and the exit flag live at the start of LDS stage 1: that stage is first
+  // written only after a barrier that every wave passes after reading the task word.
+  int* const s_task = reinterpret_cast<int*>(&lds[STAGE]);
+  int* const s_last = s_task + 1;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   const __amdgpu_buffer_rsrc_t r_act = make_rsrc(p.act, act_bytes);
 
   // tile source: one shared cursor over the list, or (with kGroups groups) this workgroup's
-  // group takes its units g, g + G, g + 2G, ... one after the other, each unit's tiles in
+  // group takes its own units (in list order) one after the other, each unit's tiles in
   // order, then the other groups' units in turn. Each group walks the list in order, so every
   // tile a Linear-2 tile waits for is taken before it by a workgroup that never waits on a
   // later tile.
@@ -118,11 +121,12 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         while (scan_group < p.ngroups) {
           const int g = (my_group + scan_group) % p.ngroups;
           const int j = __hip_atomic_load(&p.hdr[HDR_GROUP_CURSOR + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int u = g + p.ngroups * j;
-          if (u >= nunits) {
+          const int g0 = p.hdr[HDR_GROUP_OFF + g], g1 = min(p.hdr[HDR_GROUP_OFF + g + 1], nunits);
+          if (g0 + j >= g1) {
             ++scan_group;
             continue;
           }
+          const int u = p.group_units[g0 + j];
           const int lo = p.unit_start[u], hi = min(p.unit_start[u + 1], ntasks);
           const int t = atomicAdd(&p.unit_taken[u], 1);
           if (lo + t < hi) {
@@ -132,11 +136,11 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
           atomicCAS(&p.hdr[HDR_GROUP_CURSOR + g], j, j + 1);  // unit used up: move the group on
         }
       }
-      s_task = task;
+      *s_task = task;
     }
     __syncthreads();
     // the task and its m-block record are the same for the whole workgroup: keep them scalar
-    const int task = __builtin_amdgcn_readfirstlane(s_task);
+    const int task = __builtin_amdgcn_readfirstlane(*s_task);
     if (task == kNoTask) break;
     const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
     const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
@@ -333,13 +337,12 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
 
   // the last workgroup to leave resets the cursor and the ready counters, so the next
   // moe_forward on this plan starts clean without a separate launch
-  __shared__ int s_last;
   if (tid == 0) {
     const int done = __hip_atomic_fetch_add(&p.hdr[HDR_DONE], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = done == (int)gridDim.x - 1;
+    *s_last = done == (int)gridDim.x - 1;
   }
   __syncthreads();
-  if (s_last) {
+  if (*s_last) {
     const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
     for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
     const int nu = min(p.hdr[HDR_NUNITS], p.max_units);

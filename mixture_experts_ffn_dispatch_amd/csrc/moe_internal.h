@@ -22,14 +22,16 @@ enum : int {
   HDR_DONE = 7,    // persistent workgroups that have exited (the last one resets the state)
   HDR_GROUP_CURSOR = 8,   // [8, 16): units each locality group has finished
   HDR_NUNITS = 16,        // units in the unit table
+  HDR_GROUP_OFF = 17,     // [17, 26): first entry of each group's unit list (9th = end)
   HDR_SLOTS = 32
 };
 
 // Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, which is
 // the XCD it runs on (the hardware deals workgroups to the 8 XCDs round-robin). The list is
 // made of units (kUnit consecutive tiles of one run, written in blocks of kBlockM m-blocks x
-// kBlockN n-tiles of one expert); unit u belongs to group u % kGroups, so the workgroups that
-// share an XCD's L2 work on tiles of one unit, which share operand rows.
+// kBlockN n-tiles of one expert). Linear-1 units are dealt round-robin to the groups in list
+// order, and so are Linear-2 units, so every group gets an even share of both kinds of work;
+// the workgroups that share an XCD's L2 work on tiles of one unit, which share operand rows.
 constexpr int kGroups = 8;
 constexpr int kUnit = 32;
 constexpr int kBlockM = 4;
@@ -69,6 +71,7 @@ struct PlanArgs {
   int32_t* tasks;
   int32_t* unit_start;  // [max_units + 1]: list position of each unit's first tile
   int32_t* unit_taken;  // [max_units]: tiles taken from each unit in the current forward
+  int32_t* group_units; // [max_units]: each group's units in list order, groups one after another
   int max_units;
   int T, E, k, chunks, chunk_tokens;
   int W;         // experts per wave
@@ -87,6 +90,7 @@ struct GemmArgs {
   const int32_t* tasks;  // the tile list in schedule order
   const int32_t* unit_start;
   int32_t* unit_taken;
+  const int32_t* group_units;
   int max_units;
   int ngroups;  // 1: one shared cursor over the list; kGroups: each group takes its own units
   const int32_t* mb_expert;

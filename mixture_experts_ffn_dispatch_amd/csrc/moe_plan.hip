@@ -133,6 +133,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   __shared__ int s_l2s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-2 run
   __shared__ int s_l1u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-1 unit
   __shared__ int s_l2u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-2 unit
+  __shared__ int s_p1[MOE_MAX_EXPERTS + 1];   // Linear-1 units of all earlier waves
+  __shared__ int s_p2[MOE_MAX_EXPERTS + 1];   // Linear-2 units of all earlier waves
   __shared__ int s_a[MOE_MAX_EXPERTS];        // Linear-1 tiles per wave
   __shared__ int s_b[MOE_MAX_EXPERTS];        // Linear-2 tiles per wave
   const int tid = threadIdx.x;
@@ -207,6 +209,19 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   }
   __syncthreads();
   const int auw = units_of(aw), buw = units_of(bw);
+  int n_l1_units, n_l2_units;
+  {
+    const int p1 = block_exclusive_scan(tid < nw ? auw : 0, s_tmp, n_l1_units);
+    const int p2 = block_exclusive_scan(tid < nw ? buw : 0, s_tmp, n_l2_units);
+    if (tid < nw) {
+      s_p1[tid] = p1;
+      s_p2[tid] = p2;
+    }
+    if (tid == 0) {
+      s_p1[nw] = n_l1_units;
+      s_p2[nw] = n_l2_units;
+    }
+  }
   int total_units;
   if (!interleaved) {
     // Expert-Wave order: L1(0) L2(0) L1(1) L2(1) ...
@@ -271,24 +286,43 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
                     (ml - mg * kBlockM) * bn_act + (nt - ng * kBlockN);
       const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
       long long at;
-      int unit;
-      if (!interleaved || (ph == 0 && w < D)) {
+      int unit, other_before;  // other_before: units of the other phase earlier in the list
+      if (!interleaved) {
         at = (long long)(ph ? s_l2s[w] : s_l1s[w]) + q;
         unit = (ph ? s_l2u[w] : s_l1u[w]) + ur;
+        other_before = ph ? s_p1[w + 1] : s_p2[w];
+      } else if (ph == 0 && w < D) {  // lead prefix
+        at = (long long)s_l1s[w] + q;
+        unit = s_l1u[w] + ur;
+        other_before = 0;
       } else if (ph == 1) {  // Linear-2 unit ur of segment w
         const int bu = units_of(s_b[w]);
         const int au = w + D < nw ? units_of(s_a[w + D]) : 0;
         const int l1_before = au ? (int)((long long)ur * au / bu) : 0;  // all full units
         at = (long long)s_l2s[w] + (long long)(ur + l1_before) * kUnit + o;
         unit = s_l2u[w] + ur + l1_before;
+        other_before = s_p1[min(w + D, nw)] + l1_before;
       } else {  // Linear-1 unit ur of wave w, in segment w - D
         const int b = s_b[w - D], bu = units_of(b), au = units_of(s_a[w]);
         const int c = bu ? (int)(((long long)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
         at = (long long)s_l1s[w] + (long long)ur * kUnit + (c == bu ? b : c * kUnit) + o;
         unit = s_l1u[w] + ur + c;
+        other_before = s_p2[w - D] + c;
       }
       a.tasks[at] = make_task(ph, mb, nt);
-      if (o == 0) a.unit_start[unit] = (int)at;
+      if (o == 0) {
+        a.unit_start[unit] = (int)at;
+        // Units of each phase are dealt round-robin to the groups in list order: this unit is
+        // number pidx of its phase, so it goes to group pidx % G; its place in that group's list
+        // counts the group's earlier units of both phases.
+        const int pidx = (ph ? s_p2[w] : s_p1[w]) + ur;
+        const int g = pidx % kGroups;
+        const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
+        int goff = 0;
+        for (int h = 0; h < g; ++h)
+          goff += (n_l1_units - h + kGroups - 1) / kGroups + (n_l2_units - h + kGroups - 1) / kGroups;
+        a.group_units[goff + rank] = unit;
+      }
     }
   }
   if (tid == 0) a.unit_start[total_units] = total_mb * (a.n1 + a.n2);
@@ -302,6 +336,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_N2] = a.n2;
     a.hdr[HDR_DONE] = 0;
     a.hdr[HDR_NUNITS] = total_units;
+    int goff = 0;
+    for (int g = 0; g <= kGroups; ++g) {
+      a.hdr[HDR_GROUP_OFF + g] = goff;
+      goff += (n_l1_units - g + kGroups - 1) / kGroups + (n_l2_units - g + kGroups - 1) / kGroups;
+    }
     for (int g = 0; g < kGroups; ++g) a.hdr[HDR_GROUP_CURSOR + g] = 0;
   }
 }

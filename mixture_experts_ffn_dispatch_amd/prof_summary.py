@@ -6,8 +6,8 @@
 
 Counter values are averaged per kernel over the dispatches in the file. For the traffic
 summary, FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the persistent GEMM are scaled by
-what the same counters read for the plain device copy in the same run (rocclr copyBuffer,
-512 MiB read + 512 MiB written per dispatch).
+what the same counters read for the plain device copy in the same run: the largest rocclr
+copyBuffer dispatches, each copying 1 GiB (1 GiB read + 1 GiB written).
 """
 import collections
 import csv
@@ -27,9 +27,19 @@ def short(name):
 
 def counters(path):
     agg = collections.defaultdict(list)
+    copies = collections.defaultdict(list)
     for r in csv.DictReader(open(path)):
-        agg[(short(r["Kernel_Name"]), r["Counter_Name"])].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in agg.items()}
+        k = short(r["Kernel_Name"])
+        if k == "copyBuffer":
+            copies[r["Counter_Name"]].append((int(r["Grid_Size"]), float(r["Counter_Value"])))
+        else:
+            agg[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+    out = {k: sum(v) / len(v) for k, v in agg.items()}
+    for name, vals in copies.items():  # only the largest copies (the 1 GiB reference)
+        big = max(g for g, _ in vals)
+        sel = [v for g, v in vals if g == big]
+        out[("copyBuffer", name)] = sum(sel) / len(sel)
+    return out
 
 
 def main():
@@ -53,7 +63,7 @@ def main():
     elif mode == "traffic":
         fetch, write, workload, out, sha = sys.argv[2:7]
         cf, cw = counters(fetch), counters(write)
-        copy_bytes = 512 * 1024 * 1024
+        copy_bytes = 1024 * 1024 * 1024
         f_scale = copy_bytes / (cf[("copyBuffer", "FETCH_SIZE")] * 1024)
         w_scale = copy_bytes / (cw[("copyBuffer", "WRITE_SIZE")] * 1024)
         fb = cf[("gemm_persistent_kernel", "FETCH_SIZE")] * 1024 * f_scale

@@ -89,7 +89,20 @@ def read_tasks(cfg, bufs):
     n, nunits = int(hdr[2]), int(hdr[16])
     tasks = decode(ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32))
     starts = ws[L["unit_start"]:L["unit_start"] + 4 * (nunits + 1)].view(np.int32).tolist()
-    return tasks, starts, L
+    gunits = ws[L["group_units"]:L["group_units"] + 4 * nunits].view(np.int32).tolist()
+    goff = hdr[17:26].tolist()
+    return tasks, starts, gunits, goff, L
+
+
+def model_groups(units, groups=8):
+    """Units of each phase dealt round-robin to the groups in list order."""
+    seen = [0, 0]
+    lists = [[] for _ in range(groups)]
+    for u, tiles in enumerate(units):
+        ph = tiles[0][0]
+        lists[seen[ph] % groups].append(u)
+        seen[ph] += 1
+    return lists
 
 
 # long runs: several full units per run, so the unit-level merge is exercised
@@ -109,7 +122,7 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     cfg = make_cfg(shape, schedule=schedule, lead_waves=lead, tile_m=tile_m)
     note(f"task list {which} schedule={schedule} lead={lead} tile_m={tile_m}")
     b = run(cfg, dev)
-    tasks, starts, L = read_tasks(cfg, b)
+    tasks, starts, gunits, goff, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
     units = model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], shape.experts_per_wave, schedule, lead)
     assert tasks == [t for u in units for t in u]
@@ -118,6 +131,10 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     for u in units:
         expect_starts.append(expect_starts[-1] + len(u))
     assert starts == expect_starts
+    # each locality group's unit list, groups one after another
+    lists = model_groups(units)
+    assert goff == [sum(len(x) for x in lists[:g]) for g in range(9)]
+    assert gunits == [u for x in lists for u in x]
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
     seen = {}
     for ph, mb, _ in tasks:
