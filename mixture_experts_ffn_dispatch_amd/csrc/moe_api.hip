@@ -61,7 +61,8 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   const long long max_tasks = max_mblk * (n1 + n2);
   if (n1 > kTaskNtMask || n2 > kTaskNtMask) return MOE_ERR_UNSUPPORTED;
   if (max_mblk >= (1ll << kTaskMblkBits) - 1) return MOE_ERR_UNSUPPORTED;
-  if (max_tasks > 0x7FFFFFFFll || chunks * c->E > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
+  // the planner places tiles with 32-bit arithmetic on unit counts: keep the list below 2^20
+  if (max_tasks > (1ll << 20) || chunks * c->E > 0x7FFFFFFFll) return MOE_ERR_UNSUPPORTED;
   L->chunks = (int32_t)chunks;
   L->chunk_tokens = (int32_t)chunk_tokens;
   L->max_mblk = (int32_t)max_mblk;

@@ -70,7 +70,7 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW>
+template <int BM, int WN, int WM, int MINW, int PF>
 __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
@@ -222,20 +222,22 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     // Fragments alternate between two register sets so that reads for k-step s + 1 are in
     // flight while the MFMAs of k-step s run; the sched_group_barrier patterns keep the
     // compiler from sinking the reads next to their first use.
-    u32x4 stage_regs[LD];
+    // PF register sets stage K steps on their way to LDS: the loads for K step kt + PF go out
+    // while step kt is computed, so PF steps of operands are in flight per workgroup.
+    u32x4 stage_regs[PF][LD];
     bf16x8 fa[2][FN], fb[2][FM];
     const int KT = K / BK;
-    auto issue_loads = [&](int kt) {
+    auto issue_loads = [&](int kt, int set) {
 #pragma unroll
       for (int i = 0; i < LD; ++i)
-        stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(i < BN / RG ? r_w : r_t, (int)(i < BN / RG ? vbase_w : vbase_t),
-                                                              (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
+        stage_regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
+            i < BN / RG ? r_w : r_t, (int)(i < BN / RG ? vbase_w : vbase_t), (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
     };
-    auto write_lds = [&](int st) {
+    auto write_lds = [&](int st, int set) {
 #pragma unroll
       for (int i = 0; i < LD; ++i) {
         const int r = lrow + RG * i;
-        *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[i];
+        *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[set][i];
       }
     };
     auto read_frags = [&](int st, int ks, int set) {
@@ -254,17 +256,13 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         for (int m = 0; m < FM; ++m)
           acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][f], fb[set][m], acc[f][m], 0, 0, 0);
     };
-
-    issue_loads(0);
-    write_lds(0);
-    __syncthreads();
-    read_frags(0, 0, 0);
-    for (int kt = 0; kt < KT; ++kt) {
+    // one K step on LDS stage kt & 1; `load_set` receives step kt + PF, `write_set` holds kt + 1
+    auto step = [&](int kt, int load_set, int write_set) {
       const int st = kt & 1;
-      // the last K step reloads itself instead of reading past the operands (never used)
-      const int kn = kt + 1 < KT ? kt + 1 : kt;
+      // past the last K step the loads re-read the last one instead (never used)
+      const int kn = kt + PF < KT ? kt + PF : KT - 1;
       __builtin_amdgcn_sched_barrier(0);
-      issue_loads(kn);
+      issue_loads(kn, load_set);
       read_frags(st, 1, 1);
       mfmas(0);
       Interleave<FN * FM, LD, FN + FM, 0>::emit();
@@ -277,12 +275,26 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       mfmas(0);
       Interleave<FN * FM, 0, FN + FM, 0>::emit();
       __builtin_amdgcn_sched_barrier(0);
-      write_lds(st ^ 1);
+      write_lds(st ^ 1, write_set);
       mfmas(1);
       Interleave<FN * FM, 0, 0, LD>::emit();
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       read_frags(st ^ 1, 0, 0);
+    };
+
+    issue_loads(0, 0);
+    if (PF == 2) issue_loads(KT > 1 ? 1 : 0, PF - 1);
+    write_lds(0, 0);
+    __syncthreads();
+    read_frags(0, 0, 0);
+    if (PF == 1) {
+      for (int kt = 0; kt < KT; ++kt) step(kt, 0, 0);
+    } else {  // step kt loads into set kt & 1 and writes set (kt + 1) & 1
+      for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, 0, PF - 1);
+        if (kt + 1 < KT) step(kt + 1, PF - 1, 0);
+      }
     }
     __syncthreads();  // the epilogue's next task reuses both stages
 
@@ -355,9 +367,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   }
 }
 
-template <int BM, int WN, int WM, int MINW>
+template <int BM, int WN, int WM, int MINW, int PF>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -380,10 +392,10 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
   switch (tile_m) {
-    case 256: return launch_variant<256, 2, 4, 2>(a, num_workgroups, s);
-    case 128: return launch_variant<128, 2, 2, 1>(a, num_workgroups, s);
-    case 64: return launch_variant<64, 4, 1, 2>(a, num_workgroups, s);
-    case 32: return launch_variant<32, 4, 1, 2>(a, num_workgroups, s);
+    case 256: return launch_variant<256, 2, 4, 2, 2>(a, num_workgroups, s);
+    case 128: return launch_variant<128, 2, 2, 1, 1>(a, num_workgroups, s);
+    case 64: return launch_variant<64, 4, 1, 2, 1>(a, num_workgroups, s);
+    case 32: return launch_variant<32, 4, 1, 2, 1>(a, num_workgroups, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,10 +4,11 @@
 // expert (X-Stage paper, Introduction, MoE-layer paragraph); the expert-wave paragraph and
 // Section 4.2 (MegaMoE) fix the tile orders that the schedule builder writes.
 //
-//   route_hist     one block per token chunk, one wavefront per token: top-k over the E
-//                  logits (descending, ties to the lower expert id), renormalised softmax
-//                  weights, and a per-(expert, chunk) count of the routed slots (LDS atomics
-//                  on integers: order-free, exact).
+//   route_*        one block per token chunk, one wavefront per token (or one segment of
+//                  2^n >= E lanes per token when E <= 64): top-k over the E logits
+//                  (descending, ties to the lower expert id), renormalised softmax weights, and
+//                  a per-(expert, chunk) count of the routed slots (LDS atomics on integers:
+//                  order-free, exact).
 //   scan_schedule  one workgroup: exclusive scan of the expert-major count table, which gives
 //                  every (expert, chunk) its first dispatched row, the expert offsets, the
 //                  m-block table, zeroed dependency counters and the tile list.
@@ -85,6 +86,62 @@ __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
     for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);  // same on every lane
     if (lane < a.k) {
       const size_t f = (size_t)t * a.k + lane;
+      a.topk_ids[f] = my_e;
+      a.topk_w[f] = ex / sum;
+      atomicAdd(&cnt[my_e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
+}
+
+// Routing for E <= 64: one token per S-lane segment of a wavefront (S = a power of two >= E),
+// so 64 / S tokens are routed at once. Same selection and weights as route_hist_kernel; the
+// butterflies stay inside a segment (XOR with offsets below S).
+template <int S>
+__global__ __launch_bounds__(kPlanThreads) void route_small_kernel(PlanArgs a) {
+  __shared__ int cnt[MOE_MAX_EXPERTS];
+  constexpr int TPW = 64 / S;  // tokens per wavefront step
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = lane / S, sl = lane % S;
+  const int chunk = blockIdx.x;
+  for (int e = tid; e < a.E; e += kPlanThreads) cnt[e] = 0;
+  __syncthreads();
+  const int t_end = min(a.T, (chunk + 1) * a.chunk_tokens);
+  for (int t0 = chunk * a.chunk_tokens + wave * TPW; t0 < t_end; t0 += kPlanWaves * TPW) {
+    const int t = t0 + seg;
+    const bool live = t < t_end;
+    float x = live && sl < a.E ? a.logits[(size_t)t * a.E + sl] : -INFINITY;
+    x = (x != x) ? -INFINITY : x;  // NaN is not a valid logit; keep selection in range
+    bool taken = false;
+    float my_v = 0.f, top = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < a.k; ++j) {
+      const bool cand = !taken && sl < a.E;
+      float bv = cand ? x : -INFINITY;
+      int be = cand ? sl : 0x7fffffff;
+#pragma unroll
+      for (int off = S / 2; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oe = __shfl_xor(be, off);
+        if (ranks_before(ov, oe, bv, be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (be == sl) taken = true;
+      if (sl == j) {
+        my_v = bv;
+        my_e = be;
+      }
+      if (j == 0) top = bv;
+    }
+    const float ex = sl < a.k ? expf(my_v - top) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int off = S / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (live && sl < a.k) {
+      const size_t f = (size_t)t * a.k + sl;
       a.topk_ids[f] = my_e;
       a.topk_w[f] = ex / sum;
       atomicAdd(&cnt[my_e], 1);
@@ -190,7 +247,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     }
   }
   for (int i = tid; i < total_mb; i += kScanThreads) a.mb_ready[i] = 0;
-  for (int i = tid; i < a.max_units; i += kScanThreads) a.unit_taken[i] = 0;
   __syncthreads();
 
   // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
@@ -285,27 +341,29 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       const int q = (s_mb[e] - s_mb[w * W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
                     (ml - mg * kBlockM) * bn_act + (nt - ng * kBlockN);
       const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
-      long long at;
+      // positions and unit counts stay below 2^31 (the host caps the tile count), so 32-bit
+      // unsigned arithmetic is exact here
+      unsigned at;
       int unit, other_before;  // other_before: units of the other phase earlier in the list
       if (!interleaved) {
-        at = (long long)(ph ? s_l2s[w] : s_l1s[w]) + q;
+        at = (unsigned)(ph ? s_l2s[w] : s_l1s[w]) + q;
         unit = (ph ? s_l2u[w] : s_l1u[w]) + ur;
         other_before = ph ? s_p1[w + 1] : s_p2[w];
       } else if (ph == 0 && w < D) {  // lead prefix
-        at = (long long)s_l1s[w] + q;
+        at = (unsigned)s_l1s[w] + q;
         unit = s_l1u[w] + ur;
         other_before = 0;
       } else if (ph == 1) {  // Linear-2 unit ur of segment w
         const int bu = units_of(s_b[w]);
         const int au = w + D < nw ? units_of(s_a[w + D]) : 0;
-        const int l1_before = au ? (int)((long long)ur * au / bu) : 0;  // all full units
-        at = (long long)s_l2s[w] + (long long)(ur + l1_before) * kUnit + o;
+        const int l1_before = au ? (int)((unsigned)ur * au / bu) : 0;  // all full units
+        at = (unsigned)s_l2s[w] + (unsigned)(ur + l1_before) * kUnit + o;
         unit = s_l2u[w] + ur + l1_before;
         other_before = s_p1[min(w + D, nw)] + l1_before;
       } else {  // Linear-1 unit ur of wave w, in segment w - D
         const int b = s_b[w - D], bu = units_of(b), au = units_of(s_a[w]);
-        const int c = bu ? (int)(((long long)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
-        at = (long long)s_l1s[w] + (long long)ur * kUnit + (c == bu ? b : c * kUnit) + o;
+        const int c = bu ? (int)(((unsigned)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
+        at = (unsigned)s_l1s[w] + (unsigned)ur * kUnit + (c == bu ? b : c * kUnit) + o;
         unit = s_l1u[w] + ur + c;
         other_before = s_p2[w - D] + c;
       }
@@ -326,6 +384,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     }
   }
   if (tid == 0) a.unit_start[total_units] = total_mb * (a.n1 + a.n2);
+  for (int i = tid; i < total_units; i += kScanThreads) a.unit_taken[i] = 0;
   if (tid == 0) {
     a.hdr[HDR_ERROR] = 0;
     a.hdr[HDR_CURSOR] = 0;
@@ -487,7 +546,10 @@ inline int grid_rows(long long rows_per_block_units) {
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s) {
   const int R = (a.E + 63) / 64;
   const dim3 grid(a.chunks), block(kPlanThreads);
-  if (R <= 1) hipLaunchKernelGGL(route_hist_kernel<1>, grid, block, 0, s, a);
+  if (a.E <= 8) hipLaunchKernelGGL(route_small_kernel<8>, grid, block, 0, s, a);
+  else if (a.E <= 16) hipLaunchKernelGGL(route_small_kernel<16>, grid, block, 0, s, a);
+  else if (a.E <= 32) hipLaunchKernelGGL(route_small_kernel<32>, grid, block, 0, s, a);
+  else if (R <= 1) hipLaunchKernelGGL(route_small_kernel<64>, grid, block, 0, s, a);
   else if (R <= 2) hipLaunchKernelGGL(route_hist_kernel<2>, grid, block, 0, s, a);
   else if (R <= 4) hipLaunchKernelGGL(route_hist_kernel<4>, grid, block, 0, s, a);
   else if (R <= 8) hipLaunchKernelGGL(route_hist_kernel<8>, grid, block, 0, s, a);
