@@ -43,6 +43,12 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
          ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
+// 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at lds_dst + 16 L
+// (lds_dst is the same for the whole wavefront); voffset and soffset address the buffer only
+__device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, soffset, 0, 0);
+}
+
 __device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
 
 // LDS swizzle of a 128-byte operand row: its eight 16-byte chunks are permuted by XOR with
@@ -70,7 +76,7 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW, int PF>
+template <int BM, int WN, int WM, int MINW, int PF, bool DMA>
 __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
@@ -185,8 +191,11 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     // staged chunk i of this thread: weight rows for i < BN/32, token rows after; the per-lane
     // part of the byte offset is one of two bases, the rest is wave-uniform (scalar offset)
     const uint32_t rowb = (uint32_t)K * 2u;  // bytes per operand row
-    const uint32_t vbase_w = (uint32_t)((l2 ? nt * kTileN2 : nt * kTileN1) + lrow) * rowb + (uint32_t)lchunk * 16u;
-    const uint32_t vbase_t = (uint32_t)lrow * rowb + (uint32_t)lchunk * 16u;
+    // the buffer->LDS path puts lane L's 16 bytes at slot L of the wave's 1 KiB, so there the
+    // global side applies the swizzle; register staging loads chunk lchunk and swizzles on write
+    const uint32_t gchunk = (uint32_t)(DMA ? lds_pchunk : lchunk);
+    const uint32_t vbase_w = (uint32_t)((l2 ? nt * kTileN2 : nt * kTileN1) + lrow) * rowb + gchunk * 16u;
+    const uint32_t vbase_t = (uint32_t)lrow * rowb + gchunk * 16u;
     const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
     auto chunk_soff = [&](int i) -> uint32_t {
       if (i < BN / RG) {
@@ -224,9 +233,21 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     // compiler from sinking the reads next to their first use.
     // PF register sets stage K steps on their way to LDS: the loads for K step kt + PF go out
     // while step kt is computed, so PF steps of operands are in flight per workgroup.
-    u32x4 stage_regs[PF][LD];
+    u32x4 stage_regs[DMA ? 1 : PF][DMA ? 1 : LD];
     bf16x8 fa[2][FN], fb[2][FM];
     const int KT = K / BK;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    // K step kt straight into LDS stage st: wave w fills rows 8w + RG i, eight rows (1 KiB) a
+    // load. Past the last K step the offsets are pushed out of every buffer's range (bit 31;
+    // each range is below 2^31 bytes): such loads fetch nothing and fill the stage with zeros.
+    auto issue_dma = [&](int kt, int st) {
+      const uint32_t past = kt < KT ? 0u : 0x80000000u;
+      const uint32_t vw = vbase_w | past, vt = vbase_t | past;
+#pragma unroll
+      for (int i = 0; i < LD; ++i)
+        load_lds16(i < BN / RG ? r_w : r_t, &lds[st * STAGE + (wave_u * 8 + RG * i) * BK], i < BN / RG ? vw : vt,
+                   chunk_soff(i) + (uint32_t)kt * BK * 2u);
+    };
     auto issue_loads = [&](int kt, int set) {
 #pragma unroll
       for (int i = 0; i < LD; ++i)
@@ -283,6 +304,43 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       read_frags(st ^ 1, 0, 0);
     };
 
+    // buffer->LDS variant: step kt's loads land in the other stage while step kt is computed;
+    // one wait + barrier per step publishes them
+    auto step_dma = [&](int st, int kt) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_dma(kt + 1, st ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, 1, 1);
+      mfmas(0);
+      Interleave<FN * FM, 0, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, 2, 0);
+      mfmas(1);
+      Interleave<FN * FM, 0, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(st, 3, 1);
+      mfmas(0);
+      Interleave<FN * FM, 0, FN + FM, 0>::emit();
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(1);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      read_frags(st ^ 1, 0, 0);
+    };
+
+    if constexpr (DMA) {
+      issue_dma(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      read_frags(0, 0, 0);
+      int kt = 0;
+      for (; kt + 1 < KT; kt += 2) {
+        step_dma(0, kt);
+        step_dma(1, kt + 1);
+      }
+      if (kt < KT) step_dma(0, kt);
+    } else {
     issue_loads(0, 0);
     if (PF == 2) issue_loads(KT > 1 ? 1 : 0, PF - 1);
     write_lds(0, 0);
@@ -295,6 +353,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         step(kt, 0, PF - 1);
         if (kt + 1 < KT) step(kt + 1, PF - 1, 0);
       }
+    }
     }
     __syncthreads();  // the epilogue's next task reuses both stages
 
@@ -367,9 +426,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   }
 }
 
-template <int BM, int WN, int WM, int MINW, int PF>
+template <int BM, int WN, int WM, int MINW, int PF, bool DMA = false>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF, DMA>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -392,7 +451,7 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
   switch (tile_m) {
-    case 256: return launch_variant<256, 2, 4, 2, 2>(a, num_workgroups, s);
+    case 256: return launch_variant<256, 2, 4, 2, 1, true>(a, num_workgroups, s);
     case 128: return launch_variant<128, 2, 2, 1, 1>(a, num_workgroups, s);
     case 64: return launch_variant<64, 4, 1, 2, 1>(a, num_workgroups, s);
     case 32: return launch_variant<32, 4, 1, 2, 1>(a, num_workgroups, s);
