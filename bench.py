@@ -29,6 +29,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0
+HDR_LEAD = 26  # workspace header slot holding the interleave lead the plan used
 
 
 def log(*a):
@@ -119,7 +120,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dsv3_share")
     ap.add_argument("--schedule", choices=["interleaved", "expert_wave"], default="interleaved")
-    ap.add_argument("--lead", type=int, default=1)
+    ap.add_argument("--lead", type=int, default=0, help="interleave lead D (0 = chosen by the plan)")
     ap.add_argument("--tile-m", type=int, default=0)
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
@@ -194,7 +195,9 @@ def main() -> int:
         step_ms = np.array([e[0].elapsed_time(e[4]) for e in ev])
         counts = b["counts"].cpu().numpy()
         layout = moe.moe_workspace_layout(cfg)
-        return dict(wall_ms=wall * 1e3 / steps, step_ms=step_ms, per=per, counts=counts, layout=layout)
+        lead_used = int(b["ws"][:128].cpu().numpy().view(np.int32)[HDR_LEAD])
+        return dict(wall_ms=wall * 1e3 / steps, step_ms=step_ms, per=per, counts=counts, layout=layout,
+                    lead_used=lead_used)
 
     main_res = timed(args.schedule, args.steps, args.warmup)
     other = None
@@ -230,6 +233,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "lead_waves": args.lead,
+                   "lead_used": main_res["lead_used"],
                    "tile_m": main_res["layout"]["tile_m"], "seed": s.seed},
         "roofline": {"bound": "mfma", "kernel": "gemm_persistent_kernel", "achieved": round(achieved, 3),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),

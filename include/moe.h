@@ -64,6 +64,14 @@ enum {
   MOE_SCHED_INTERLEAVED = 1
 };
 
+/* Lead chosen by moe_plan when lead_waves is 0 (interleaved order): a Linear-2 tile of wave w
+   should be taken only after the last Linear-1 tile of wave w has finished. With G persistent
+   workgroups, list positions are taken at about G per mean tile duration, and each lead wave
+   beyond the first places about one wave of tiles between the two. Tile durations scale with
+   their K (H for Linear-1, I for Linear-2), so with A Linear-1 and B Linear-2 tiles over nw
+   waves:  D = 1 + ceil(G * H * nw / (A * H + B * I)), clamped to [1, nw]. The lead only
+   reorders tiles; results do not depend on it. */
+
 /* Limits of this implementation (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 1024 /* E                                        */
 #define MOE_MAX_TOPK 32      /* k                                        */
@@ -77,7 +85,7 @@ typedef struct moe_config {
   int32_t k;                /* experts per token (1..min(E, 32))                                 */
   int32_t experts_per_wave; /* W >= 1; wave w holds experts [w*W, min(E, (w+1)*W))              */
   int32_t schedule;         /* MOE_SCHED_*                                                       */
-  int32_t lead_waves;       /* interleaved order only: D >= 1 (0 means 1); ignored otherwise    */
+  int32_t lead_waves;       /* interleaved order only: D >= 1, or 0 = chosen by moe_plan (below) */
   int32_t num_workgroups;   /* persistent grid; 0 or more than fits at once = every resident slot */
   int32_t tile_m;           /* rows per GEMM tile: 0 = chosen from T*k/E, else 32, 64, 128, 256 */
   int32_t spin_limit;       /* bounded-wait iterations of a Linear-2 tile; 0 = default (~seconds)*/

@@ -171,10 +171,13 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.chunk_tokens = L.chunk_tokens;
   a.W = cfg->experts_per_wave > cfg->E ? cfg->E : cfg->experts_per_wave;
   a.schedule = cfg->schedule;
-  a.lead = cfg->lead_waves > 0 ? cfg->lead_waves : 1;
+  a.lead = cfg->lead_waves;
   a.tile_m = L.tile_m;
   a.n1 = L.n1_tiles;
   a.n2 = L.n2_tiles;
+  a.H = cfg->H;
+  a.I = cfg->I;
+  if (gemm_grid(L.tile_m, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_scan_schedule(a, s) != hipSuccess) return MOE_ERR_HIP;

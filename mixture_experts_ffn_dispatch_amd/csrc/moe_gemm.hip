@@ -128,14 +128,18 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
           const int g = (my_group + scan_group) % p.ngroups;
           const int j = __hip_atomic_load(&p.hdr[HDR_GROUP_CURSOR + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           const int g0 = p.hdr[HDR_GROUP_OFF + g], g1 = min(p.hdr[HDR_GROUP_OFF + g + 1], nunits);
-          if (g0 + j >= g1) {
+          if (g0 < 0 || g0 + j >= g1) {
             ++scan_group;
             continue;
           }
           const int u = p.group_units[g0 + j];
+          if ((unsigned)u >= (unsigned)nunits) {  // a plan this workspace could not have produced
+            atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
+            break;
+          }
           const int lo = p.unit_start[u], hi = min(p.unit_start[u + 1], ntasks);
           const int t = atomicAdd(&p.unit_taken[u], 1);
-          if (lo + t < hi) {
+          if (lo >= 0 && lo + t < hi) {
             task = p.tasks[lo + t];
             break;
           }
@@ -151,11 +155,13 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
     const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
     const int nt = task & kTaskNtMask;
-    const int e = __builtin_amdgcn_readfirstlane(p.mb_expert[mb]);
-    const int row0 = __builtin_amdgcn_readfirstlane(p.mb_row0[mb]);
-    const int nrows = __builtin_amdgcn_readfirstlane(p.mb_rows[mb]);
+    // the m-block record is read only for an index inside the table
+    const bool mb_ok = mb < p.max_mblk;
+    const int e = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_expert[mb]) : -1;
+    const int row0 = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_row0[mb]) : 0;
+    const int nrows = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_rows[mb]) : 0;
     // a plan this workspace could not have produced: skip the tile, report, never fault
-    if (mb >= p.max_mblk || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
+    if (!mb_ok || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
         nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1)) {
       if (tid == 0) atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
       __syncthreads();
@@ -427,7 +433,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
 }
 
 template <int BM, int WN, int WM, int MINW, int PF, bool DMA = false>
-hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
+hipError_t variant_grid(int num_workgroups, int* grid) {
   auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF, DMA>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
@@ -440,7 +446,17 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
   err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NT, 0);
   if (err != hipSuccess) return err;
   const int capacity = cus * (per_cu > 0 ? per_cu : 1);
-  int grid = num_workgroups > 0 && num_workgroups < capacity ? num_workgroups : capacity;
+  *grid = num_workgroups > 0 && num_workgroups < capacity ? num_workgroups : capacity;
+  return hipSuccess;
+}
+
+template <int BM, int WN, int WM, int MINW, int PF, bool DMA = false>
+hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF, DMA>;
+  constexpr int NT = 64 * WN * WM;
+  int grid = 0;
+  hipError_t err = variant_grid<BM, WN, WM, MINW, PF, DMA>(num_workgroups, &grid);
+  if (err != hipSuccess) return err;
   GemmArgs g = a;
   g.ngroups = grid >= kGroups ? kGroups : 1;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, s, g);
@@ -455,6 +471,16 @@ hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStr
     case 128: return launch_variant<128, 2, 2, 1, 1>(a, num_workgroups, s);
     case 64: return launch_variant<64, 4, 1, 2, 1>(a, num_workgroups, s);
     case 32: return launch_variant<32, 4, 1, 2, 1>(a, num_workgroups, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid) {
+  switch (tile_m) {
+    case 256: return variant_grid<256, 2, 4, 2, 1, true>(num_workgroups, grid);
+    case 128: return variant_grid<128, 2, 2, 1, 1>(num_workgroups, grid);
+    case 64: return variant_grid<64, 4, 1, 2, 1>(num_workgroups, grid);
+    case 32: return variant_grid<32, 4, 1, 2, 1>(num_workgroups, grid);
     default: return hipErrorInvalidValue;
   }
 }

@@ -23,6 +23,8 @@ enum : int {
   HDR_GROUP_CURSOR = 8,   // [8, 16): units each locality group has finished
   HDR_NUNITS = 16,        // units in the unit table
   HDR_GROUP_OFF = 17,     // [17, 26): first entry of each group's unit list (9th = end)
+  HDR_LEAD = 26,          // interleave lead the plan used (0 for the Expert-Wave order)
+  HDR_PLAN_GRID = 27,     // GEMM grid size the plan assumed when it chose the lead
   HDR_SLOTS = 32
 };
 
@@ -76,8 +78,10 @@ struct PlanArgs {
   int T, E, k, chunks, chunk_tokens;
   int W;         // experts per wave
   int schedule;  // MOE_SCHED_*
-  int lead;      // interleave lead (>= 1)
+  int lead;      // interleave lead (>= 1), or 0: chosen from the tile counts
   int tile_m, n1, n2;
+  int H, I;      // Linear-1 K = H, Linear-2 K = I (tile durations scale with them)
+  int grid;      // persistent GEMM workgroups (tiles in flight)
 };
 
 struct GemmArgs {
@@ -115,5 +119,7 @@ hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd
                           int H, int k, hipStream_t s);
 // Persistent grouped GEMM; grid = num_workgroups (0 = CUs x occupancy).
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s);
+// The grid launch_gemm uses for this tile height and request (every workgroup resident at once).
+hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid);
 
 }  // namespace moe

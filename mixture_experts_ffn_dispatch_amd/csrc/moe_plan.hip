@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   //    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
   //    last unit may be shorter); the orders are defined on units, so every unit is one
   //    contiguous stretch of the list holding tiles of a single run.
-  const int W = a.W, nw = (E + W - 1) / W, D = a.lead;
+  const int W = a.W, nw = (E + W - 1) / W;
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
   int aw = 0, bw = 0;
   if (tid < nw) {
@@ -264,6 +264,25 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     s_b[tid] = bw;
   }
   __syncthreads();
+  // Lead 0 picks D from the tile counts. A Linear-2 tile of wave i must not be taken before
+  // the last Linear-1 tile of wave i has finished. With `grid` tiles in flight, list
+  // positions are taken at about grid per mean tile duration, so that takes about
+  // grid * t1 / t_mean positions (t1, t2: Linear-1 / Linear-2 tile durations, proportional
+  // to their K = H and I). Each lead wave beyond the first puts about one wave of tiles,
+  // (A + B) / nw, between them (A, B: Linear-1 / Linear-2 tiles in all waves). Hence
+  //   D = 1 + ceil(grid * H * nw / (A * H + B * I)),  clamped to [1, nw].
+  int D = a.lead;
+  {
+    int A, B;
+    block_exclusive_scan(aw, s_tmp, A);
+    block_exclusive_scan(bw, s_tmp, B);
+    if (interleaved && D == 0) {
+      const long long den = (long long)A * a.H + (long long)B * a.I;
+      const long long num = (long long)a.grid * a.H * nw;
+      D = den > 0 ? 1 + (int)min((num + den - 1) / den, (long long)nw) : 1;
+    }
+    D = min(max(D, 1), max(nw, 1));
+  }
   const int auw = units_of(aw), buw = units_of(bw);
   int n_l1_units, n_l2_units;
   {
@@ -395,6 +414,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_N2] = a.n2;
     a.hdr[HDR_DONE] = 0;
     a.hdr[HDR_NUNITS] = total_units;
+    a.hdr[HDR_LEAD] = interleaved ? D : 0;
+    a.hdr[HDR_PLAN_GRID] = a.grid;
     int goff = 0;
     for (int g = 0; g <= kGroups; ++g) {
       a.hdr[HDR_GROUP_OFF + g] = goff;

@@ -114,7 +114,19 @@ def long_workload():
     return Device(W.generate(LONG))
 
 
-@pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9)])
+def auto_lead(counts, tile_m, n1, n2, W_, H, I, grid):
+    """The lead moe_plan picks for lead_waves = 0: D = 1 + ceil(G*H*nw / (A*H + B*I)) over nw
+    waves with A Linear-1 and B Linear-2 tiles and G persistent workgroups, in [1, nw]."""
+    E = len(counts)
+    nw = -(-E // W_)
+    mblocks = sum(-(-int(c) // tile_m) for c in counts)
+    A, B = mblocks * n1, mblocks * n2
+    den = A * H + B * I
+    D = 1 + min(-(-(grid * H * nw) // den), nw) if den > 0 else 1
+    return min(max(D, 1), max(nw, 1))
+
+
+@pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9), (1, 0)])
 @pytest.mark.parametrize("tile_m", [32, 128])
 @pytest.mark.parametrize("which", ["short", "long"])
 def test_task_list_matches_model(workload, long_workload, which, schedule, lead, tile_m):
@@ -124,6 +136,18 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     b = run(cfg, dev)
     tasks, starts, gunits, goff, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
+    hdr = b["ws"][:128].cpu().numpy().view(np.int32)
+    used_lead, grid = int(hdr[26]), int(hdr[27])
+    if schedule == moe.MOE_SCHED_EXPERT_WAVE:
+        assert used_lead == 0
+    elif lead > 0:
+        nw = -(-shape.E // shape.experts_per_wave)
+        assert used_lead == min(lead, nw)
+    else:
+        assert grid >= 1
+        assert used_lead == auto_lead(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], shape.experts_per_wave,
+                                      shape.H, shape.I, grid)
+        lead = used_lead
     units = model_order(counts, L["tile_m"], L["n1_tiles"], L["n2_tiles"], shape.experts_per_wave, schedule, lead)
     assert tasks == [t for u in units for t in u]
     # the unit table marks where each unit starts, the last entry is the list length
