@@ -5,8 +5,9 @@
 // (I -> H); MegaMoE runs these stages inside one persistent kernel, grouped into expert waves,
 // and Section 4.2 reorders independent Linear-1 / Linear-2 tiles across waves. Here:
 //
-//  * A workgroup (4 wavefronts) takes the next tile from the list with one atomic increment,
-//    so tiles start in list order whatever the grid size.
+//  * A workgroup (8 wavefronts for 256-row tiles, 4 for smaller ones) takes the next tile of
+//    its XCD group's part of the list (unit cursor + per-unit counter), so each group's tiles
+//    start in list order whatever the grid size.
 //  * Linear-1 tile (expert e, m-block, n-tile): 128 gate rows + the matching 128 up rows of
 //    W1[e] against up to tile_m dispatched rows; the epilogue forms
 //    A = bf16(silu(gate) * up) for 128 columns and releases the m-block's ready counter.
@@ -14,8 +15,9 @@
 //    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
 //  * The MFMA A operand is the weight tile and the B operand the token tile, so one lane
 //    ends with four consecutive output columns of one token row (8-byte stores).
-//  * Operands are staged through LDS in 64-wide K steps, double buffered, the 16-byte chunks
-//    of each row XOR-swizzled so that 128-bit fragment reads are free of bank conflicts.
+//  * Operands go from global memory straight into LDS (buffer->LDS loads) in 64-wide K steps,
+//    double buffered, the 16-byte chunks of each row XOR-swizzled so that 128-bit fragment
+//    reads are free of bank conflicts.
 //  * Every output element accumulates its K products in the same order (ascending K steps of
 //    16 inside one v_mfma_f32_32x32x16_bf16 chain), so tile order, grid size and tile height
 //    never change a result bit.
@@ -28,7 +30,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
@@ -76,7 +77,7 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW, int PF, bool DMA>
+template <int BM, int WN, int WM, int MINW>
 __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
-  const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, chunk
+  const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, LDS chunk slot
   const int lds_pchunk = lchunk ^ swz(lrow);    // swizzled chunk (rows RG apart swizzle alike)
   const int fr_row = lane & 31, fr_chunk = lane >> 5;
 
@@ -194,12 +195,12 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       r_w = make_rsrc(p.w1 + (size_t)e * 2 * p.I * p.H, (uint32_t)((size_t)2 * p.I * p.H * 2));
       r_t = make_rsrc(p.xd + (size_t)row0 * p.H, (uint32_t)((size_t)nrows * p.H * 2));
     }
-    // staged chunk i of this thread: weight rows for i < BN/32, token rows after; the per-lane
+    // staged chunk i of this thread: weight rows for i < BN/RG, token rows after; the per-lane
     // part of the byte offset is one of two bases, the rest is wave-uniform (scalar offset)
     const uint32_t rowb = (uint32_t)K * 2u;  // bytes per operand row
-    // the buffer->LDS path puts lane L's 16 bytes at slot L of the wave's 1 KiB, so there the
-    // global side applies the swizzle; register staging loads chunk lchunk and swizzles on write
-    const uint32_t gchunk = (uint32_t)(DMA ? lds_pchunk : lchunk);
+    // the buffer->LDS load puts lane L's 16 bytes at slot L of the wave's 1 KiB, so the global
+    // side applies the swizzle: the lane owning LDS chunk slot p of row r loads chunk p ^ swz(r)
+    const uint32_t gchunk = (uint32_t)lds_pchunk;
     const uint32_t vbase_w = (uint32_t)((l2 ? nt * kTileN2 : nt * kTileN1) + lrow) * rowb + gchunk * 16u;
     const uint32_t vbase_t = (uint32_t)lrow * rowb + gchunk * 16u;
     const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
@@ -229,43 +230,29 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     }
 
     // Mainloop, software-pipelined by hand. Per K step of 64 (four MFMA k-steps of 16):
-    //   k-step 0 MFMAs | the next K step's global loads + fragments of k-step 1
+    //   the next K step's operands go straight into the other LDS stage (buffer->LDS loads)
+    //   k-step 0 MFMAs | fragments of k-step 1
     //   k-step 1 MFMAs | fragments of k-step 2
     //   k-step 2 MFMAs | fragments of k-step 3
-    //   k-step 3 MFMAs | the next K step written into the other LDS stage
-    //   barrier, then fragments of the next K step's k-step 0
+    //   k-step 3 MFMAs
+    //   wait for this wave's loads, barrier (the other stage is complete, this one free), then
+    //   fragments of the next K step's k-step 0
     // Fragments alternate between two register sets so that reads for k-step s + 1 are in
     // flight while the MFMAs of k-step s run; the sched_group_barrier patterns keep the
     // compiler from sinking the reads next to their first use.
-    // PF register sets stage K steps on their way to LDS: the loads for K step kt + PF go out
-    // while step kt is computed, so PF steps of operands are in flight per workgroup.
-    u32x4 stage_regs[DMA ? 1 : PF][DMA ? 1 : LD];
     bf16x8 fa[2][FN], fb[2][FM];
     const int KT = K / BK;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // K step kt straight into LDS stage st: wave w fills rows 8w + RG i, eight rows (1 KiB) a
     // load. Past the last K step the offsets are pushed out of every buffer's range (bit 31;
     // each range is below 2^31 bytes): such loads fetch nothing and fill the stage with zeros.
-    auto issue_dma = [&](int kt, int st) {
+    auto issue_loads = [&](int kt, int st) {
       const uint32_t past = kt < KT ? 0u : 0x80000000u;
       const uint32_t vw = vbase_w | past, vt = vbase_t | past;
 #pragma unroll
       for (int i = 0; i < LD; ++i)
         load_lds16(i < BN / RG ? r_w : r_t, &lds[st * STAGE + (wave_u * 8 + RG * i) * BK], i < BN / RG ? vw : vt,
                    chunk_soff(i) + (uint32_t)kt * BK * 2u);
-    };
-    auto issue_loads = [&](int kt, int set) {
-#pragma unroll
-      for (int i = 0; i < LD; ++i)
-        stage_regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(
-            i < BN / RG ? r_w : r_t, (int)(i < BN / RG ? vbase_w : vbase_t), (int)(chunk_soff(i) + (uint32_t)kt * BK * 2u), 0);
-    };
-    auto write_lds = [&](int st, int set) {
-#pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        const int r = lrow + RG * i;
-        *reinterpret_cast<u32x4*>(&lds[st * STAGE + r * BK + lds_pchunk * 8]) = stage_regs[set][i];
-      }
     };
     auto read_frags = [&](int st, int ks, int set) {
       const uint16_t* base = &lds[st * STAGE];
@@ -283,38 +270,11 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         for (int m = 0; m < FM; ++m)
           acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][f], fb[set][m], acc[f][m], 0, 0, 0);
     };
-    // one K step on LDS stage kt & 1; `load_set` receives step kt + PF, `write_set` holds kt + 1
-    auto step = [&](int kt, int load_set, int write_set) {
-      const int st = kt & 1;
-      // past the last K step the loads re-read the last one instead (never used)
-      const int kn = kt + PF < KT ? kt + PF : KT - 1;
+    // one K step on LDS stage st (a constant at each call site); K step kt + 1 lands in the
+    // other stage meanwhile
+    auto step = [&](int st, int kt) {
       __builtin_amdgcn_sched_barrier(0);
-      issue_loads(kn, load_set);
-      read_frags(st, 1, 1);
-      mfmas(0);
-      Interleave<FN * FM, LD, FN + FM, 0>::emit();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, 2, 0);
-      mfmas(1);
-      Interleave<FN * FM, 0, FN + FM, 0>::emit();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, 3, 1);
-      mfmas(0);
-      Interleave<FN * FM, 0, FN + FM, 0>::emit();
-      __builtin_amdgcn_sched_barrier(0);
-      write_lds(st ^ 1, write_set);
-      mfmas(1);
-      Interleave<FN * FM, 0, 0, LD>::emit();
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
-      read_frags(st ^ 1, 0, 0);
-    };
-
-    // buffer->LDS variant: step kt's loads land in the other stage while step kt is computed;
-    // one wait + barrier per step publishes them
-    auto step_dma = [&](int st, int kt) {
-      __builtin_amdgcn_sched_barrier(0);
-      issue_dma(kt + 1, st ^ 1);
+      issue_loads(kt + 1, st ^ 1);
       __builtin_amdgcn_sched_barrier(0);
       read_frags(st, 1, 1);
       mfmas(0);
@@ -335,32 +295,17 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       read_frags(st ^ 1, 0, 0);
     };
 
-    if constexpr (DMA) {
-      issue_dma(0, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      read_frags(0, 0, 0);
-      int kt = 0;
-      for (; kt + 1 < KT; kt += 2) {
-        step_dma(0, kt);
-        step_dma(1, kt + 1);
-      }
-      if (kt < KT) step_dma(0, kt);
-    } else {
     issue_loads(0, 0);
-    if (PF == 2) issue_loads(KT > 1 ? 1 : 0, PF - 1);
-    write_lds(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     read_frags(0, 0, 0);
-    if (PF == 1) {
-      for (int kt = 0; kt < KT; ++kt) step(kt, 0, 0);
-    } else {  // step kt loads into set kt & 1 and writes set (kt + 1) & 1
-      for (int kt = 0; kt < KT; kt += 2) {
-        step(kt, 0, PF - 1);
-        if (kt + 1 < KT) step(kt + 1, PF - 1, 0);
-      }
+    // two K steps per trip, so the stage index is a constant and the body one basic block
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+      step(0, kt);
+      step(1, kt + 1);
     }
-    }
+    if (kt < KT) step(0, kt);
     __syncthreads();  // the epilogue's next task reuses both stages
 
     // epilogue: lane holds, for output block (f, m), rows 8g + 4*(lane>>5) + {0..3} of the
@@ -432,9 +377,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   }
 }
 
-template <int BM, int WN, int WM, int MINW, int PF, bool DMA = false>
+template <int BM, int WN, int WM, int MINW>
 hipError_t variant_grid(int num_workgroups, int* grid) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF, DMA>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -450,12 +395,12 @@ hipError_t variant_grid(int num_workgroups, int* grid) {
   return hipSuccess;
 }
 
-template <int BM, int WN, int WM, int MINW, int PF, bool DMA = false>
+template <int BM, int WN, int WM, int MINW>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, PF, DMA>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
   constexpr int NT = 64 * WN * WM;
   int grid = 0;
-  hipError_t err = variant_grid<BM, WN, WM, MINW, PF, DMA>(num_workgroups, &grid);
+  hipError_t err = variant_grid<BM, WN, WM, MINW>(num_workgroups, &grid);
   if (err != hipSuccess) return err;
   GemmArgs g = a;
   g.ngroups = grid >= kGroups ? kGroups : 1;
@@ -467,20 +412,20 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
   switch (tile_m) {
-    case 256: return launch_variant<256, 2, 4, 2, 1, true>(a, num_workgroups, s);
-    case 128: return launch_variant<128, 2, 2, 1, 1>(a, num_workgroups, s);
-    case 64: return launch_variant<64, 4, 1, 2, 1>(a, num_workgroups, s);
-    case 32: return launch_variant<32, 4, 1, 2, 1>(a, num_workgroups, s);
+    case 256: return launch_variant<256, 2, 4, 2>(a, num_workgroups, s);
+    case 128: return launch_variant<128, 2, 2, 1>(a, num_workgroups, s);
+    case 64: return launch_variant<64, 4, 1, 2>(a, num_workgroups, s);
+    case 32: return launch_variant<32, 4, 1, 2>(a, num_workgroups, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid) {
   switch (tile_m) {
-    case 256: return variant_grid<256, 2, 4, 2, 1, true>(num_workgroups, grid);
-    case 128: return variant_grid<128, 2, 2, 1, 1>(num_workgroups, grid);
-    case 64: return variant_grid<64, 4, 1, 2, 1>(num_workgroups, grid);
-    case 32: return variant_grid<32, 4, 1, 2, 1>(num_workgroups, grid);
+    case 256: return variant_grid<256, 2, 4, 2>(num_workgroups, grid);
+    case 128: return variant_grid<128, 2, 2, 1>(num_workgroups, grid);
+    case 64: return variant_grid<64, 4, 1, 2>(num_workgroups, grid);
+    case 32: return variant_grid<32, 4, 1, 2>(num_workgroups, grid);
     default: return hipErrorInvalidValue;
   }
 }
