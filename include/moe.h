@@ -14,6 +14,7 @@
  * The four calls follow the stages: moe_plan (route + expert histogram + prefix scan +
  * stable scatter + tile schedule), moe_dispatch (gather rows), moe_forward (persistent grouped
  * GEMM: Linear-1 with fused SwiGLU, then Linear-2), moe_combine (router-weighted sum).
+ * moe_forward_gather is moe_dispatch + moe_forward in one launch (rows gathered on load).
  *
  * Conventions for every call:
  *   - bfloat16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
@@ -191,6 +192,17 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
 moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t* w1,
                        const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws,
                        size_t ws_bytes, void* stream);
+
+/* moe_forward with the dispatch folded into Linear-1's operand loads (the MegaMoE kernel of the
+ * X-Stage paper's Introduction fuses dispatch into its persistent kernel): a Linear-1 tile
+ * reads token row perm[r] / k of x for dispatched row r, so no xd buffer is written or read.
+ *   rt  routing from moe_plan (reads rt->perm); x [T, H] bf16 token rows
+ *   w1, w2, act, yd, ws as for moe_forward.
+ * act, yd (and so the combined output) are byte-identical to moe_dispatch + moe_forward.
+ * MOE_ERR_INVALID_ARG if rt, rt->perm or x is NULL; otherwise as moe_forward. */
+moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, const uint16_t* x,
+                              const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* Combine: out[t, :] = bf16( sum_{j=0..k-1} topk_w[t, j] * yd[pos[t*k + j], :] ), fp32 sum in
  * ascending j (fixed order, no atomics, deterministic).

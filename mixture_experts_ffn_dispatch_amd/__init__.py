@@ -10,7 +10,7 @@ from __future__ import annotations
 from ._lib import (  # noqa: F401
     MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
     MOE_FLAG_FORCE_WAIT_TIMEOUT, MOE_OK, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, LIB_PATH,
-    MoeConfig, MoeError, abi_version, load, moe_combine, moe_dispatch, moe_forward, moe_plan,
+    MoeConfig, MoeError, abi_version, load, moe_combine, moe_dispatch, moe_forward, moe_forward_gather, moe_plan,
     moe_status_read, moe_workspace_layout, moe_workspace_size, strerror,
 )
 
@@ -31,24 +31,29 @@ def alloc_routing(cfg: MoeConfig, device="cuda") -> dict:
     )
 
 
-def alloc_buffers(cfg: MoeConfig, device="cuda") -> dict:
-    """Routing buffers, workspace and the row buffers (xd, act, yd) plus the output."""
+def alloc_buffers(cfg: MoeConfig, device="cuda", xd=True) -> dict:
+    """Routing buffers, workspace and the row buffers (xd unless ``xd=False``, act, yd) plus
+    the output."""
     import torch
 
     R = cfg.T * cfg.k
     bf = dict(dtype=torch.bfloat16, device=device)
     b = alloc_routing(cfg, device)
     b["ws"] = torch.zeros(moe_workspace_size(cfg), dtype=torch.uint8, device=device)
-    b["xd"] = torch.empty((R, cfg.H), **bf)
+    b["xd"] = torch.empty((R, cfg.H), **bf) if xd else None
     b["act"] = torch.empty((R, cfg.I), **bf)
     b["yd"] = torch.empty((R, cfg.H), **bf)
     b["out"] = torch.empty((cfg.T, cfg.H), **bf)
     return b
 
 
-def run_layer(cfg: MoeConfig, bufs: dict, x, logits, w1, w2, stream=None) -> None:
-    """plan -> dispatch -> forward -> combine on one stream (asynchronous)."""
+def run_layer(cfg: MoeConfig, bufs: dict, x, logits, w1, w2, stream=None, gather=False) -> None:
+    """plan -> dispatch -> forward -> combine on one stream (asynchronous); with ``gather``,
+    plan -> forward_gather (dispatch folded into the Linear-1 loads) -> combine."""
     moe_plan(cfg, logits, bufs, bufs["ws"], stream)
-    moe_dispatch(cfg, bufs, x, bufs["xd"], stream)
-    moe_forward(cfg, bufs["xd"], w1, w2, bufs["act"], bufs["yd"], bufs["ws"], stream)
+    if gather:
+        moe_forward_gather(cfg, bufs, x, w1, w2, bufs["act"], bufs["yd"], bufs["ws"], stream)
+    else:
+        moe_dispatch(cfg, bufs, x, bufs["xd"], stream)
+        moe_forward(cfg, bufs["xd"], w1, w2, bufs["act"], bufs["yd"], bufs["ws"], stream)
     moe_combine(cfg, bufs, bufs["yd"], bufs["out"], stream)

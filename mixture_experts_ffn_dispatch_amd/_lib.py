@@ -100,6 +100,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "moe_plan": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, ctypes.c_size_t, vp]),
         "moe_dispatch": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
         "moe_forward": (ctypes.c_int32, [P(CConfig), vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "moe_forward_gather": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                                                vp]),
         "moe_combine": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
         "moe_status_read": (ctypes.c_int32, [vp, ctypes.c_size_t, vp]),
     }
@@ -184,6 +186,12 @@ def moe_dispatch(cfg, rt: dict, x, xd, stream=None) -> None:
 def moe_forward(cfg, xd, w1, w2, act, yd, ws, stream=None) -> None:
     _check(load().moe_forward(ctypes.byref(_cfg(cfg)), _ptr(xd), _ptr(w1), _ptr(w2), _ptr(act), _ptr(yd),
                               _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_forward_gather(cfg, rt: dict, x, w1, w2, act, yd, ws, stream=None) -> None:
+    _check(load().moe_forward_gather(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(x), _ptr(w1), _ptr(w2),
+                                     _ptr(act), _ptr(yd), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward_gather")
 
 
 def moe_combine(cfg, rt: dict, yd, out, stream=None) -> None:

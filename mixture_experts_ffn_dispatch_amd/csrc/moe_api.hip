@@ -195,15 +195,23 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t* w1, const uint16_t* w2,
-                       uint16_t* act, uint16_t* yd, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+// shared by moe_forward (rows from xd) and moe_forward_gather (rows from x through perm)
+moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_t* x, const int32_t* perm,
+                        const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws,
+                        size_t ws_bytes, void* stream) {
   moe_ws_layout L;
   moe_status st = compute_layout(cfg, &L);
   if (st != MOE_OK) return st;
-  if (!xd || !w1 || !w2 || !act || !yd || !ws) return MOE_ERR_INVALID_ARG;
+  if ((!xd && !(x && perm)) || !w1 || !w2 || !act || !yd || !ws) return MOE_ERR_INVALID_ARG;
   if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
   GemmArgs g;
   g.xd = xd;
+  g.x = x;
+  g.perm = perm;
+  g.T = cfg->T;
+  g.k = cfg->k;
+  g.gather = xd ? 0 : 1;
   g.w1 = w1;
   g.w2 = w2;
   g.act = act;
@@ -231,6 +239,20 @@ moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_gemm(g, L.tile_m, cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_forward(const moe_config* cfg, const uint16_t* xd, const uint16_t* w1, const uint16_t* w2,
+                       uint16_t* act, uint16_t* yd, void* ws, size_t ws_bytes, void* stream) {
+  if (!xd) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, xd, nullptr, nullptr, w1, w2, act, yd, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, const uint16_t* x, const uint16_t* w1,
+                              const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!rt || !rt->perm || !x) return MOE_ERR_INVALID_ARG;
+  return forward_impl(cfg, nullptr, x, rt->perm, w1, w2, act, yd, ws, ws_bytes, stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd, uint16_t* out,

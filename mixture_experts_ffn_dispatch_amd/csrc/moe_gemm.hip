@@ -193,23 +193,39 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       r_t = make_rsrc(p.act + (size_t)row0 * p.I, (uint32_t)((size_t)nrows * p.I * 2));
     } else {
       r_w = make_rsrc(p.w1 + (size_t)e * 2 * p.I * p.H, (uint32_t)((size_t)2 * p.I * p.H * 2));
-      r_t = make_rsrc(p.xd + (size_t)row0 * p.H, (uint32_t)((size_t)nrows * p.H * 2));
+      r_t = p.gather ? make_rsrc(p.x, (uint32_t)((size_t)p.T * p.H * 2))
+                     : make_rsrc(p.xd + (size_t)row0 * p.H, (uint32_t)((size_t)nrows * p.H * 2));
     }
-    // staged chunk i of this thread: weight rows for i < BN/RG, token rows after; the per-lane
-    // part of the byte offset is one of two bases, the rest is wave-uniform (scalar offset)
+    // staged chunk i of this thread: weight rows for i < BN/RG (per-lane base + wave-uniform
+    // row offset), token rows after (one per-lane offset per row group)
     const uint32_t rowb = (uint32_t)K * 2u;  // bytes per operand row
     // the buffer->LDS load puts lane L's 16 bytes at slot L of the wave's 1 KiB, so the global
     // side applies the swizzle: the lane owning LDS chunk slot p of row r loads chunk p ^ swz(r)
     const uint32_t gchunk = (uint32_t)lds_pchunk;
     const uint32_t vbase_w = (uint32_t)((l2 ? nt * kTileN2 : nt * kTileN1) + lrow) * rowb + gchunk * 16u;
-    const uint32_t vbase_t = (uint32_t)lrow * rowb + gchunk * 16u;
+    // token rows lrow + RG j: contiguous rows of the m-block, or (Linear-1 with gather) row
+    // perm[r] / k of x, the dispatch folded into the load; rows past the m-block, or with a
+    // routing entry out of range, get an offset outside the buffer and read as zero
+    constexpr int TG = BM / RG;
+    uint32_t vtok[TG];
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      const int r = lrow + RG * j;
+      if (p.gather && !l2) {
+        int src = -1;
+        if (r < nrows) {
+          const int f = p.perm[row0 + r];
+          src = (unsigned)f < (unsigned)p.R ? f / p.k : -1;
+        }
+        vtok[j] = src >= 0 ? (uint32_t)src * rowb + gchunk * 16u : 0x80000000u;
+      } else {
+        vtok[j] = (uint32_t)r * rowb + gchunk * 16u;
+      }
+    }
     const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
     auto chunk_soff = [&](int i) -> uint32_t {
-      if (i < BN / RG) {
-        if (l2) return (uint32_t)i * RG * rowb;
-        return i < BN / (2 * RG) ? (uint32_t)i * RG * rowb : up_off + (uint32_t)(i - BN / (2 * RG)) * RG * rowb;
-      }
-      return (uint32_t)(i - BN / RG) * RG * rowb;
+      if (l2) return (uint32_t)i * RG * rowb;
+      return i < BN / (2 * RG) ? (uint32_t)i * RG * rowb : up_off + (uint32_t)(i - BN / (2 * RG)) * RG * rowb;
     };
 
     f32x16 acc[FN][FM];
@@ -244,15 +260,18 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const int KT = K / BK;
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     // K step kt straight into LDS stage st: wave w fills rows 8w + RG i, eight rows (1 KiB) a
-    // load. Past the last K step the offsets are pushed out of every buffer's range (bit 31;
-    // each range is below 2^31 bytes): such loads fetch nothing and fill the stage with zeros.
+    // load. Past the last K step the offsets get bit 31 set, which is outside every buffer
+    // range below 2^31 bytes: such loads fetch nothing. (A larger weight slab would read bytes
+    // of its own buffer into a stage that is never used.)
     auto issue_loads = [&](int kt, int st) {
       const uint32_t past = kt < KT ? 0u : 0x80000000u;
-      const uint32_t vw = vbase_w | past, vt = vbase_t | past;
+      const uint32_t vw = vbase_w | past;
 #pragma unroll
-      for (int i = 0; i < LD; ++i)
-        load_lds16(i < BN / RG ? r_w : r_t, &lds[st * STAGE + (wave_u * 8 + RG * i) * BK], i < BN / RG ? vw : vt,
-                   chunk_soff(i) + (uint32_t)kt * BK * 2u);
+      for (int i = 0; i < LD; ++i) {
+        uint16_t* dst = &lds[st * STAGE + (wave_u * 8 + RG * i) * BK];
+        if (i < BN / RG) load_lds16(r_w, dst, vw, chunk_soff(i) + (uint32_t)kt * BK * 2u);
+        else load_lds16(r_t, dst, vtok[i - BN / RG] | past, (uint32_t)kt * BK * 2u);
+      }
     };
     auto read_frags = [&](int st, int ks, int set) {
       const uint16_t* base = &lds[st * STAGE];

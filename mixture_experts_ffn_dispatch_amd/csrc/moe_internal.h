@@ -85,7 +85,10 @@ struct PlanArgs {
 };
 
 struct GemmArgs {
-  const uint16_t* xd;
+  const uint16_t* xd;      // dispatched rows [R, H], or unused when gather is set
+  const uint16_t* x;       // token rows [T, H] (gather): Linear-1 reads row perm[r] / k for row r
+  const int32_t* perm;     // [R] (gather)
+  int T, k, gather;
   const uint16_t* w1;
   const uint16_t* w2;
   uint16_t* act;

@@ -38,9 +38,12 @@ class Device:
         self.w2 = dev_bf16(data["w2"])
 
 
-def run(cfg: moe.MoeConfig, dev: Device, bufs: dict | None = None, check_status: bool = True) -> dict:
-    bufs = bufs or moe.alloc_buffers(cfg)
-    moe.run_layer(cfg, bufs, dev.x, dev.logits, dev.w1, dev.w2)
+def run(cfg: moe.MoeConfig, dev: Device, bufs: dict | None = None, check_status: bool = True,
+        gather: bool = False) -> dict:
+    """The layer through the C ABI: plan, dispatch, forward, combine; with ``gather`` the
+    dispatch is folded into the forward (moe_forward_gather) and no xd buffer exists."""
+    bufs = bufs or moe.alloc_buffers(cfg, xd=not gather)
+    moe.run_layer(cfg, bufs, dev.x, dev.logits, dev.w1, dev.w2, gather=gather)
     if check_status:
         st = moe.moe_status_read(bufs["ws"])
         assert st == moe.MOE_OK, moe.strerror(st)

@@ -89,6 +89,10 @@ def test_null_pointers_rejected_before_any_launch():
     assert lib.moe_dispatch(ctypes.byref(c), ctypes.byref(rt), None, None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_forward(ctypes.byref(c), None, None, None, None, None, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(c), ctypes.byref(rt), None, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_gather(ctypes.byref(c), ctypes.byref(rt), None, None, None, None, None, None, 0,
+                                  None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_gather(ctypes.byref(c), None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+                                  1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_status_read(None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size(None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size(ctypes.byref(c), None) == moe.MOE_ERR_INVALID_ARG
@@ -103,3 +107,5 @@ def test_undersized_workspace_rejected():
     assert lib.moe_plan(ctypes.byref(c), dummy, ctypes.byref(rt), dummy, need - 1, None) == moe.MOE_ERR_WORKSPACE
     assert lib.moe_forward(ctypes.byref(c), dummy, dummy, dummy, dummy, dummy, dummy, need - 1, None) == \
         moe.MOE_ERR_WORKSPACE
+    assert lib.moe_forward_gather(ctypes.byref(c), ctypes.byref(rt), dummy, dummy, dummy, dummy, dummy, dummy,
+                                  need - 1, None) == moe.MOE_ERR_WORKSPACE

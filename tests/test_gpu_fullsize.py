@@ -30,6 +30,11 @@ def test_full_size_sampled_parity(name):
     b2 = run(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev)
     for key in ("act", "yd", "out"):
         assert torch.equal(b[key].view(torch.int16), b2[key].view(torch.int16)), key
+    note("  gpu run (interleaved order, dispatch folded into the Linear-1 loads)")
+    b3 = run(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev, gather=True)
+    for key in ("act", "yd", "out"):
+        assert torch.equal(b2[key].view(torch.int16), b3[key].view(torch.int16)), key
+    del b3
 
     note("  oracle routing")
     ids, w = R.route(d["logits"], s.k)

@@ -40,12 +40,13 @@ def check_full(g, o, xd_bits, E):
 @pytest.mark.parametrize("k", [1, 2])
 @pytest.mark.parametrize("tile_m", [32, 64, 128, 256])
 @pytest.mark.parametrize("schedule", [moe.MOE_SCHED_EXPERT_WAVE, moe.MOE_SCHED_INTERLEAVED])
-def test_exact_integer_case_bit_exact(k, tile_m, schedule):
-    note(f"exact-integer k={k} tile_m={tile_m} schedule={schedule}")
+@pytest.mark.parametrize("gather", [False, True])
+def test_exact_integer_case_bit_exact(k, tile_m, schedule, gather):
+    note(f"exact-integer k={k} tile_m={tile_m} schedule={schedule} gather={gather}")
     c = V.exact_integer_case(T=100, H=256, I=192, E=4, k=k, seed=3)
     cfg = moe.MoeConfig(T=100, H=256, I=192, E=4, k=k, experts_per_wave=1, schedule=schedule, tile_m=tile_m)
     dev = Device(c)
-    b = run(cfg, dev)
+    b = run(cfg, dev, gather=gather)
     g = fetch(b)
     ex = c["expected"]
     np.testing.assert_array_equal(g["topk_ids"], ex["ids"])
@@ -89,10 +90,16 @@ def test_shape_sweep_full_parity(T, H, I, E, k, Wv, tile_m, schedule):
         d["logits"][:, E // 2:] -= 30.0
     o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], k)
     cfg = make_cfg(s, tile_m=tile_m, schedule=schedule)
-    b = run(cfg, Device(d))
+    dev = Device(d)
+    b = run(cfg, dev)
     check_full(fetch(b), o, host_bits(b["xd"]), E)
     if E >= 16:
         assert (o["counts"] == 0).any()
+    # the dispatch folded into the Linear-1 loads gives the same bytes
+    note("  gather path")
+    bg = run(cfg, dev, gather=True)
+    for key in ("act", "yd", "out"):
+        assert torch.equal(b[key].view(torch.int16), bg[key].view(torch.int16)), key
 
 
 def test_identical_experts_match_dense_ffn():
