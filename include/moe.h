@@ -118,7 +118,8 @@ typedef struct moe_ws_layout {
                            [6] L2 n-tiles per m-block, [7] exited workgroups,
                            [8..15] units finished by each locality group,
                            [16] units in the unit table, [17..25] group unit lists */
-  size_t chunk_counts;  /* int32[E * chunks]: per-(expert, token chunk) counts, then bases */
+  size_t chunk_counts;  /* int32[E * ((chunks + 3) & ~3)]: per-(expert, token chunk) counts, then each
+                           chunk's first row among its expert's rows */
   size_t mblk_expert;   /* int32[max_mblk]                                        */
   size_t mblk_row0;     /* int32[max_mblk]                                        */
   size_t mblk_rows;     /* int32[max_mblk]                                        */

@@ -76,7 +76,7 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->header = off;
   off = align_up(off + HDR_SLOTS * 4, 256);
   L->chunk_counts = off;
-  off = align_up(off + (size_t)chunks * c->E * 4, 256);
+  off = align_up(off + (size_t)((chunks + 3) & ~3ll) * c->E * 4, 256);
   L->mblk_expert = off;
   off = align_up(off + (size_t)max_mblk * 4, 256);
   L->mblk_row0 = off;
@@ -168,6 +168,7 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.E = cfg->E;
   a.k = cfg->k;
   a.chunks = L.chunks;
+  a.cstride = (L.chunks + 3) & ~3;
   a.chunk_tokens = L.chunk_tokens;
   a.W = cfg->experts_per_wave > cfg->E ? cfg->E : cfg->experts_per_wave;
   a.schedule = cfg->schedule;

@@ -65,7 +65,7 @@ struct PlanArgs {
   int32_t* perm;
   int32_t* pos;
   int32_t* hdr;
-  int32_t* chunk_counts;  // [E][chunks]
+  int32_t* chunk_counts;  // [E][cstride]: entries [0, chunks) of each row are used
   int32_t* mb_expert;
   int32_t* mb_row0;
   int32_t* mb_rows;
@@ -76,6 +76,7 @@ struct PlanArgs {
   int32_t* group_units; // [max_units]: each group's units in list order, groups one after another
   int max_units;
   int T, E, k, chunks, chunk_tokens;
+  int cstride;   // row stride of chunk_counts: chunks rounded up to a multiple of 4 (16 B)
   int W;         // experts per wave
   int schedule;  // MOE_SCHED_*
   int lead;      // interleave lead (>= 1), or 0: chosen from the tile counts

@@ -9,8 +9,9 @@
 //                  (descending, ties to the lower expert id), renormalised softmax weights, and
 //                  a per-(expert, chunk) count of the routed slots (LDS atomics on integers:
 //                  order-free, exact).
-//   scan_schedule  one workgroup: exclusive scan of the expert-major count table, which gives
-//                  every (expert, chunk) its first dispatched row, the expert offsets, the
+//   scan_schedule  one workgroup: per-expert exclusive scans of the count table (one
+//                  wavefront per expert row), which give every (expert, chunk) its first row
+//                  within the expert and every expert its count; the expert offsets, the
 //                  m-block table, zeroed dependency counters and the tile list.
 //   scatter        one block per chunk, its slots split into 16 consecutive runs, one per
 //                  wavefront: per-run expert counts, a per-expert prefix over the runs, then
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
+  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.cstride + chunk] = cnt[e];
 }
 
 // Routing for E <= 64: one token per S-lane segment of a wavefront (S = a power of two >= E),
@@ -148,10 +149,12 @@ __global__ __launch_bounds__(kPlanThreads) void route_small_kernel(PlanArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.chunks + chunk] = cnt[e];
+  for (int e = tid; e < a.E; e += kPlanThreads) a.chunk_counts[(size_t)e * a.cstride + chunk] = cnt[e];
 }
 
 constexpr int kScanThreads = 1024;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMbExpertLds = 8192;  // m-blocks whose expert the tile placement looks up in LDS
 
 __device__ inline int units_of(int tiles) { return (tiles + kUnit - 1) / kUnit; }
 
@@ -185,6 +188,10 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
 __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a) {
   __shared__ int s_tmp[32];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];  // expert offsets
+  __shared__ int s_cnt[MOE_MAX_EXPERTS];      // rows routed to each expert
+  __shared__ short s_mbe[kMbExpertLds];       // expert of each m-block (when they all fit)
+  __shared__ short s_wave[MOE_MAX_EXPERTS];    // wave of each expert
+  __shared__ int s_goff[kGroups + 1];          // first entry of each group's unit list
   __shared__ int s_mb[MOE_MAX_EXPERTS + 1];   // first m-block of each expert
   __shared__ int s_l1s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-1 run
   __shared__ int s_l2s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-2 run
@@ -197,44 +204,71 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   const int tid = threadIdx.x;
   const int E = a.E, BM = a.tile_m;
 
-  // 1. exclusive scan of the expert-major (expert, chunk) count table, in place: entry
-  //    (e, c) becomes the first dispatched row of chunk c's slots routed to expert e
-  constexpr int IT = 8;
-  const int n = E * a.chunks;
-  int carry = 0;
-  for (int base = 0; base < n; base += kScanThreads * IT) {
-    int vals[IT];
-    int sum = 0;
-    const int i0 = base + tid * IT;
+  // 1. per-expert exclusive scans of the (expert, chunk) count table, in place: entry (e, c)
+  //    becomes the first row of chunk c's slots among expert e's rows (the scatter adds the
+  //    expert's offset), and the row total is the expert's count. Wavefront w owns rows
+  //    w, w + 16, ...; each row is cut into segments of 256 entries (4 consecutive per lane,
+  //    one 16-byte access each way; rows are padded to a multiple of 4 entries, the padding
+  //    reads as zero), with a shuffle scan across the lanes. A wavefront loads up to 8
+  //    segments before scanning them, so their load latencies overlap.
+  {
+    constexpr int SEG = 256, BATCH = 8, NW = kScanThreads / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int segs_row = (a.chunks + SEG - 1) / SEG;
+    const int rows_w = wave < E ? (E - wave + NW - 1) / NW : 0;
+    const int nseg = rows_w * segs_row;
+    int run = 0;
+    for (int s0 = 0; s0 < nseg; s0 += BATCH) {
+      int v[BATCH][4];
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      vals[i] = i0 + i < n ? a.chunk_counts[i0 + i] : 0;
-      sum += vals[i];
-    }
-    int tot;
-    int run = carry + block_exclusive_scan(sum, s_tmp, tot);
+      for (int b = 0; b < BATCH; ++b) {
+        const int sg = s0 + b;
+        const int e = wave + NW * (sg / segs_row), i0 = (sg % segs_row) * SEG + lane * 4;
+        i32x4 q = {0, 0, 0, 0};
+        if (sg < nseg && i0 < a.cstride) q = *reinterpret_cast<const i32x4*>(a.chunk_counts + (size_t)e * a.cstride + i0);
 #pragma unroll
-    for (int i = 0; i < IT; ++i) {
-      const int idx = i0 + i;
-      if (idx < n) {
-        a.chunk_counts[idx] = run;
-        if (idx % a.chunks == 0) s_off[idx / a.chunks] = run;
+        for (int i = 0; i < 4; ++i) v[b][i] = i0 + i < a.chunks ? q[i] : 0;
       }
-      run += vals[i];
+#pragma unroll
+      for (int b = 0; b < BATCH; ++b) {
+        const int sg = s0 + b;
+        if (sg >= nseg) break;
+        const int e = wave + NW * (sg / segs_row), c0 = (sg % segs_row) * SEG, i0 = c0 + lane * 4;
+        if (c0 == 0) run = 0;
+        const int sum = v[b][0] + v[b][1] + v[b][2] + v[b][3];
+        int x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int y = __shfl_up(x, off);
+          if (lane >= off) x += y;
+        }
+        int r = run + x - sum;  // exclusive prefix of this lane's first entry
+        i32x4 q;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q[i] = r;
+          r += v[b][i];
+        }
+        if (i0 < a.cstride) *reinterpret_cast<i32x4*>(a.chunk_counts + (size_t)e * a.cstride + i0) = q;
+        run += __shfl(x, 63);
+        if (c0 + SEG >= a.chunks && lane == 0) s_cnt[e] = run;
+      }
     }
-    carry += tot;
   }
-  if (tid == 0) s_off[E] = carry;  // = T * k
   __syncthreads();
 
   // 2. counts, offsets and the m-block table
-  for (int e = tid; e <= E; e += kScanThreads) a.offsets[e] = s_off[e];
-  int cnt = 0, nmb = 0;
+  int cnt = 0, nmb = 0, off_total;
   if (tid < E) {
-    cnt = s_off[tid + 1] - s_off[tid];
+    cnt = s_cnt[tid];
     nmb = (cnt + BM - 1) / BM;
     a.counts[tid] = cnt;
   }
+  const int eoff = block_exclusive_scan(tid < E ? cnt : 0, s_tmp, off_total);
+  if (tid < E) s_off[tid] = eoff;
+  if (tid == 0) s_off[E] = off_total;  // = T * k
+  __syncthreads();
+  for (int e = tid; e <= E; e += kScanThreads) a.offsets[e] = s_off[e];
   int total_mb;
   const int mb0 = block_exclusive_scan(nmb, s_tmp, total_mb);
   if (tid < E) s_mb[tid] = mb0;
@@ -244,6 +278,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       a.mb_expert[mb0 + i] = tid;
       a.mb_row0[mb0 + i] = s_off[tid] + i * BM;
       a.mb_rows[mb0 + i] = min(BM, cnt - i * BM);
+      if (mb0 + i < kMbExpertLds) s_mbe[mb0 + i] = (short)tid;
     }
   }
   for (int i = tid; i < total_mb; i += kScanThreads) a.mb_ready[i] = 0;
@@ -334,26 +369,44 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       }
     }
   }
+  // first entry of each locality group's unit list (group g gets units g, g + G, ... of each
+  // phase), and the wave of each expert
+  if (tid <= kGroups) {
+    int goff = 0;
+    for (int h = 0; h < tid; ++h)
+      goff += (n_l1_units - h + kGroups - 1) / kGroups + (n_l2_units - h + kGroups - 1) / kGroups;
+    s_goff[tid] = goff;
+  }
+  for (int e = tid; e < E; e += kScanThreads) s_wave[e] = (short)(e / W);
   __syncthreads();
 
   // 4. write the tile list and the unit table. Inside a run the tiles of each expert are cut
   //    into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted block by block
   //    (m-block major inside a block), so neighbouring positions share operand rows. Every
   //    tile of a phase is placed independently: tile u of the phase is (m-block u / n, n-tile
-  //    u % n); its expert is found by binary search over s_mb. In a merged segment, Linear-1
+  //    u % n); its expert comes from the m-block table in LDS (or a binary search over s_mb
+  //    when there are more m-blocks than the table holds). In a merged segment, Linear-1
   //    unit v goes right after Linear-2 unit ceil((v+1) * bu / au) (bu, au: unit counts), which
   //    spreads the Linear-1 units evenly and ends the segment with the last Linear-1 unit.
   for (int ph = 0; ph < 2; ++ph) {
     const int n = ph ? a.n2 : a.n1;
+    // tile u = (m-block u / n, n-tile u % n), stepped by kScanThreads without dividing again
+    const int dmb = kScanThreads / n, dnt = kScanThreads % n;
+    int mb = tid / n, nt = tid % n;
     for (int u = tid; u < total_mb * n; u += kScanThreads) {
-      const int mb = u / n, nt = u % n;
-      int lo = 0, hi = E - 1;  // expert e with s_mb[e] <= mb < s_mb[e + 1]
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_mb[mid] <= mb) lo = mid;
-        else hi = mid - 1;
+      int e;  // expert e with s_mb[e] <= mb < s_mb[e + 1]
+      if (total_mb <= kMbExpertLds) {
+        e = s_mbe[mb];
+      } else {
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (s_mb[mid] <= mb) lo = mid;
+          else hi = mid - 1;
+        }
+        e = lo;
       }
-      const int e = lo, w = e / W;
+      const int w = s_wave[e];
       const int nmb = s_mb[e + 1] - s_mb[e], ml = mb - s_mb[e];
       const int mg = ml / kBlockM, ng = nt / kBlockN;
       const int bm_act = min(kBlockM, nmb - mg * kBlockM), bn_act = min(kBlockN, n - ng * kBlockN);
@@ -395,10 +448,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
         const int pidx = (ph ? s_p2[w] : s_p1[w]) + ur;
         const int g = pidx % kGroups;
         const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
-        int goff = 0;
-        for (int h = 0; h < g; ++h)
-          goff += (n_l1_units - h + kGroups - 1) / kGroups + (n_l2_units - h + kGroups - 1) / kGroups;
-        a.group_units[goff + rank] = unit;
+        a.group_units[s_goff[g] + rank] = unit;
+      }
+      mb += dmb;
+      nt += dnt;
+      if (nt >= n) {
+        nt -= n;
+        ++mb;
       }
     }
   }
@@ -416,11 +472,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_NUNITS] = total_units;
     a.hdr[HDR_LEAD] = interleaved ? D : 0;
     a.hdr[HDR_PLAN_GRID] = a.grid;
-    int goff = 0;
-    for (int g = 0; g <= kGroups; ++g) {
-      a.hdr[HDR_GROUP_OFF + g] = goff;
-      goff += (n_l1_units - g + kGroups - 1) / kGroups + (n_l2_units - g + kGroups - 1) / kGroups;
-    }
+    for (int g = 0; g <= kGroups; ++g) a.hdr[HDR_GROUP_OFF + g] = s_goff[g];
     for (int g = 0; g < kGroups; ++g) a.hdr[HDR_GROUP_CURSOR + g] = 0;
   }
 }
@@ -469,7 +521,8 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
   rank_run<false>(a, f0, f1, run[wave]);  // counts of this wave's slots per expert
   __syncthreads();
   for (int e = tid; e < a.E; e += kPlanThreads) {
-    int r = a.chunk_counts[(size_t)e * a.chunks + chunk];  // chunk's first row of expert e
+    // chunk's first row of expert e: the expert's offset plus its rows in earlier chunks
+    int r = a.offsets[e] + a.chunk_counts[(size_t)e * a.cstride + chunk];
     for (int w = 0; w < kPlanWaves; ++w) {
       const int c = run[w][e];
       run[w][e] = r;
