@@ -31,6 +31,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 
@@ -327,42 +328,59 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     if (kt < KT) step(0, kt);
     __syncthreads();  // the epilogue's next task reuses both stages
 
-    // epilogue: lane holds, for output block (f, m), rows 8g + 4*(lane>>5) + {0..3} of the
-    // weight fragment (output columns) at token column lane & 31
+    // Epilogue through LDS (both stages are free after the mainloop's last barrier), so that
+    // global stores cover whole row segments instead of 8 bytes of 32 rows per instruction.
+    // The tile's output is OC columns per token row (Linear-2: 256 of Yd; Linear-1: 128 of A,
+    // SwiGLU applied), staged row-major with the 16-byte chunks of row r XOR-swizzled by
+    // r mod (chunks per row). A lane holds, for output block (f, m), columns
+    // 8g + 4*(lane>>5) + {0..3} of the weight fragment at token row lane & 31.
+    {
+      const int OC = l2 ? BN : BN / 2;  // output columns of the tile
+      const int CPR = OC / 8;           // 16-byte chunks per row (32 or 16)
+      uint8_t* const obuf = reinterpret_cast<uint8_t*>(lds);
+      auto obuf_off = [&](int row, int chunk) -> int { return row * OC * 2 + ((chunk ^ (row & (CPR - 1))) << 4); };
 #pragma unroll
-    for (int m = 0; m < FM; ++m) {
-      const int tok = wm * (BM / WM) + m * 32 + fr_row;
-      if (tok >= nrows) continue;
-      const uint32_t grow = (uint32_t)(row0 + tok);
-      if (l2) {
+      for (int m = 0; m < FM; ++m) {
+        const int tok = wm * (BM / WM) + m * 32 + fr_row;
+        if (l2) {
 #pragma unroll
-        for (int f = 0; f < FN; ++f)
+          for (int f = 0; f < FN; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = nt * kTileN2 + wn * (BN / WN) + f * 32 + g * 8 + fr_chunk * 4;
-            if (n < p.H) {
+            for (int g = 0; g < 4; ++g) {
+              const int col = wn * (BN / WN) + f * 32 + g * 8;  // + 4 * fr_chunk
               u32x2 v;
               v.x = pack_bf16(acc[f][m][4 * g + 0], acc[f][m][4 * g + 1]);
               v.y = pack_bf16(acc[f][m][4 * g + 2], acc[f][m][4 * g + 3]);
-              __builtin_amdgcn_raw_buffer_store_b64(v, r_yd, (int)((grow * (uint32_t)p.H + (uint32_t)n) * 2u), 0, 0);
+              *reinterpret_cast<u32x2*>(obuf + obuf_off(tok, col >> 3) + fr_chunk * 8) = v;
             }
-          }
-      } else {
+        } else {
 #pragma unroll
-        for (int f = 0; f < FN / 2; ++f)
+          for (int f = 0; f < FN / 2; ++f)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int n = nt * kTileN1 + wn * (BN / 2 / WN) + f * 32 + g * 8 + fr_chunk * 4;
-            if (n < p.I) {
+            for (int g = 0; g < 4; ++g) {
+              const int col = wn * (BN / 2 / WN) + f * 32 + g * 8;
               float a4[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) a4[q] = silu(acc[f][m][4 * g + q]) * acc[f + FN / 2][m][4 * g + q];
               u32x2 v;
               v.x = pack_bf16(a4[0], a4[1]);
               v.y = pack_bf16(a4[2], a4[3]);
-              __builtin_amdgcn_raw_buffer_store_b64(v, r_act, (int)((grow * (uint32_t)p.I + (uint32_t)n) * 2u), 0, 0);
+              *reinterpret_cast<u32x2*>(obuf + obuf_off(tok, col >> 3) + fr_chunk * 8) = v;
             }
-          }
+        }
+      }
+      __syncthreads();
+      // thread t stores chunk t % CPR of rows t / CPR, + NT / CPR, ...: a wavefront writes whole
+      // row segments; rows past the m-block and columns past the matrix are not stored
+      const int ldim = l2 ? p.H : p.I;
+      const int col0 = l2 ? nt * kTileN2 : nt * kTileN1;
+      const int c = tid % CPR, col = col0 + c * 8;
+      const __amdgpu_buffer_rsrc_t r_out = l2 ? r_yd : r_act;
+      if (col < ldim) {  // ldim is a multiple of 64, so a chunk is wholly inside or outside
+        for (int r = tid / CPR; r < nrows && r < BM; r += NT / CPR) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + obuf_off(r, c));
+          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, (int)(((uint32_t)(row0 + r) * (uint32_t)ldim + (uint32_t)col) * 2u), 0, 0);
+        }
       }
     }
 
