@@ -211,6 +211,35 @@ moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, cons
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd,
                        uint16_t* out, void* stream);
 
+/* ---- Burst-Gap calibration (X-Stage paper, Section 3: the Burst-Gap microbenchmarks) ----
+ * K producers each store a burst of B bytes, then compute for a gap G, for P periods; the
+ * page measures the sender-visible issue time and the period to fit the backpressure-free
+ * issue time, the effective drain rate and the effective outstanding capacity. This runs the
+ * benchmark against the GPU's own memory (the page's local-memory control). */
+typedef struct moe_burst_cfg {
+  int32_t producers;  /* K: concurrent producer workgroups, 1 .. number of CUs (one per CU)   */
+  int32_t bytes;      /* B: bytes each producer stores per burst, a multiple of 4096, <= 2^30  */
+  int32_t periods;    /* P: bursts per producer, 1 .. 65536                                     */
+  int32_t reserved0;  /* must be 0                                                              */
+  int64_t gap_ticks;  /* G in ticks of the real-time counter (moe_burst_clock_hz), 0 .. 10^6   */
+} moe_burst_cfg;
+
+/* Runs the benchmark on `stream` (asynchronous). The buffer is split into K equal regions; each
+ * producer's bursts rotate through its region (a region far larger than the caches makes the
+ * stores drain to memory). times[(w * P + p) * 2 + 0] / [+ 1] receive, for producer w and
+ * period p, the real-time counter when the producer starts the burst and when all of its
+ * wavefronts have issued their last store (nothing waits for the stores); the gap is a busy wait
+ * from the second reading.
+ *   buf   device buffer of buf_bytes >= K * B bytes (its contents are overwritten)
+ *   times device int64 [K * P * 2]
+ * MOE_ERR_INVALID_ARG for a NULL pointer, a field outside its range or a buffer too small;
+ * MOE_ERR_HIP if the device query or the launch fails. */
+moe_status moe_burst_gap(const moe_burst_cfg* cfg, void* buf, size_t buf_bytes, int64_t* times,
+                         void* stream);
+
+/* Frequency of the real-time counter used by moe_burst_gap, in Hz (a device attribute). */
+moe_status moe_burst_clock_hz(int64_t* hz);
+
 /* Synchronises `stream`, then returns the device-side error recorded in the workspace since
  * the last moe_plan: MOE_OK, MOE_ERR_TIMEOUT (a bounded wait expired), or
  * MOE_ERR_WORKSPACE (moe_forward found a tile that no moe_plan for this cfg could have written

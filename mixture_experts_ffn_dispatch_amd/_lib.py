@@ -49,6 +49,11 @@ class CLayout(ctypes.Structure):
             "n2_tiles")]
 
 
+class CBurstCfg(ctypes.Structure):
+    _fields_ = [("producers", ctypes.c_int32), ("bytes", ctypes.c_int32), ("periods", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("gap_ticks", ctypes.c_int64)]
+
+
 @dataclass
 class MoeConfig:
     """Python mirror of ``moe_config``."""
@@ -104,6 +109,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                                 vp]),
         "moe_combine": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
         "moe_status_read": (ctypes.c_int32, [vp, ctypes.c_size_t, vp]),
+        "moe_burst_gap": (ctypes.c_int32, [P(CBurstCfg), vp, ctypes.c_size_t, vp, vp]),
+        "moe_burst_clock_hz": (ctypes.c_int32, [P(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -197,6 +204,18 @@ def moe_forward_gather(cfg, rt: dict, x, w1, w2, act, yd, ws, stream=None) -> No
 def moe_combine(cfg, rt: dict, yd, out, stream=None) -> None:
     _check(load().moe_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(yd), _ptr(out),
                               _stream(stream)), "moe_combine")
+
+
+def moe_burst_gap(producers: int, nbytes: int, periods: int, gap_ticks: int, buf, times, stream=None) -> None:
+    c = CBurstCfg(producers=producers, bytes=nbytes, periods=periods, reserved0=0, gap_ticks=gap_ticks)
+    _check(load().moe_burst_gap(ctypes.byref(c), _ptr(buf), buf.numel() * buf.element_size(), _ptr(times),
+                                _stream(stream)), "moe_burst_gap")
+
+
+def moe_burst_clock_hz() -> int:
+    hz = ctypes.c_int64(0)
+    _check(load().moe_burst_clock_hz(ctypes.byref(hz)), "moe_burst_clock_hz")
+    return int(hz.value)
 
 
 def moe_status_read(ws, stream=None) -> int:

@@ -111,6 +111,33 @@ extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
 
+moe_status moe_burst_clock_hz(int64_t* hz) {
+  if (!hz) return MOE_ERR_INVALID_ARG;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return MOE_ERR_HIP;
+  *hz = (int64_t)khz * 1000;
+  return MOE_OK;
+}
+
+moe_status moe_burst_gap(const moe_burst_cfg* c, void* buf, size_t buf_bytes, int64_t* times, void* stream) {
+  if (!c || !buf || !times) return MOE_ERR_INVALID_ARG;
+  if (c->reserved0 != 0 || c->periods < 1 || c->periods > 65536) return MOE_ERR_INVALID_ARG;
+  if (c->bytes < 4096 || c->bytes % 4096 != 0 || c->bytes > (1 << 30)) return MOE_ERR_INVALID_ARG;
+  if (c->gap_ticks < 0 || c->gap_ticks > 1000000) return MOE_ERR_INVALID_ARG;
+  if (c->producers < 1) return MOE_ERR_INVALID_ARG;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MOE_ERR_HIP;
+  if (c->producers > cus) return MOE_ERR_INVALID_ARG;
+  const size_t region = buf_bytes / (size_t)c->producers / (size_t)c->bytes * (size_t)c->bytes;
+  if (region < (size_t)c->bytes) return MOE_ERR_INVALID_ARG;
+  if (launch_burst_gap(static_cast<uint8_t*>(buf), region, c->producers, c->bytes, c->periods, (long long)c->gap_ticks,
+                       reinterpret_cast<long long*>(times), static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
 const char* moe_strerror(moe_status s) {
   switch (s) {
     case MOE_OK: return "success";

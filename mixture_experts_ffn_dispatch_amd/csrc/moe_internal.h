@@ -125,5 +125,9 @@ hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s);
 // The grid launch_gemm uses for this tile height and request (every workgroup resident at once).
 hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid);
+// Burst-Gap microbenchmark: `producers` workgroups, each storing `bytes` per burst into its own
+// `region` of buf, `periods` times, with a busy gap of `gap_ticks` real-time counter ticks.
+hipError_t launch_burst_gap(uint8_t* buf, size_t region, int producers, int bytes, int periods,
+                            long long gap_ticks, long long* times, hipStream_t s);
 
 }  // namespace moe

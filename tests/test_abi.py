@@ -94,6 +94,8 @@ def test_null_pointers_rejected_before_any_launch():
     assert lib.moe_forward_gather(ctypes.byref(c), None, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
                                   1 << 30, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_status_read(None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_burst_gap(None, None, 0, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_burst_clock_hz(None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size(None, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_workspace_size(ctypes.byref(c), None) == moe.MOE_ERR_INVALID_ARG
 
