@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes. */
 typedef enum {
@@ -113,11 +113,13 @@ typedef struct moe_routing {
    base; all int32 arrays). Filled on the host by moe_workspace_layout. */
 typedef struct moe_ws_layout {
   size_t total_bytes;   /* = moe_workspace_size                                     */
-  size_t header;        /* int32[32]: [0] error code, [1] task cursor, [2] task count,
+  size_t header;        /* int32[64]: [0] error code, [1] task cursor, [2] task count,
                            [3] m-block count, [4] tile_m, [5] L1 n-tiles per m-block,
                            [6] L2 n-tiles per m-block, [7] exited workgroups,
-                           [8..15] units finished by each locality group,
-                           [16] units in the unit table, [17..25] group unit lists */
+                           [8..15] records handed out from each locality group's list,
+                           [16] units in the unit table, [17..25] group unit lists,
+                           [26] interleave lead used, [27] GEMM grid the plan assumed,
+                           [32..40] group record lists (first record of group g, 9th = end) */
   size_t chunk_counts;  /* int32[E * ((chunks + 3) & ~3)]: per-(expert, token chunk) counts, then each
                            chunk's first row among its expert's rows */
   size_t mblk_expert;   /* int32[max_mblk]                                        */
@@ -129,14 +131,18 @@ typedef struct moe_ws_layout {
   size_t unit_start;    /* int32[max_tasks + 1]: list position of each unit's first tile
                            (a unit: up to 32 consecutive tiles of one wave's Linear-1 or
                            Linear-2 run; header[16] holds the unit count)           */
-  size_t unit_taken;    /* int32[max_tasks]: tiles taken from each unit by moe_forward */
   size_t group_units;   /* int32[max_tasks]: the units of locality group 0 in list order,
                            then those of group 1, ... (group g: entries
                            [header[17+g], header[18+g]))                           */
+  size_t group_tasks;   /* int32[max_slots][4]: each group's units in its order, 32 record
+                           slots per unit holding its tiles as (task word, expert, first
+                           dispatched row, rows), spare slots 0x7FFFFFFE (no-op);
+                           group g: slots [header[32+g], header[33+g])             */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;
   int32_t max_tasks;
+  int32_t max_slots;    /* record slots of the group lists                        */
   int32_t tile_m;       /* rows per tile                                          */
   int32_t tile_n1;      /* Linear-1 tile: output columns of A per tile (gate+up = 2x weight rows) */
   int32_t tile_n2;      /* Linear-2 tile: output columns of Yd per tile            */

@@ -44,8 +44,8 @@ class CRouting(ctypes.Structure):
 class CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
-        "tasks", "unit_start", "unit_taken", "group_units")] + [(n, ctypes.c_int32) for n in (
-            "chunks", "chunk_tokens", "max_mblk", "max_tasks", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
+        "tasks", "unit_start", "group_units", "group_tasks")] + [(n, ctypes.c_int32) for n in (
+            "chunks", "chunk_tokens", "max_mblk", "max_tasks", "max_slots", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
             "n2_tiles")]
 
 

@@ -89,10 +89,14 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   off = align_up(off + (size_t)max_tasks * 4, 256);
   L->unit_start = off;
   off = align_up(off + ((size_t)max_tasks + 1) * 4, 256);
-  L->unit_taken = off;
-  off = align_up(off + (size_t)max_tasks * 4, 256);
   L->group_units = off;
   off = align_up(off + (size_t)max_tasks * 4, 256);
+  // group record lists: kUnit slots per unit; a run of t tiles has ceil(t / kUnit) units and
+  // there are at most 2 E runs (each wave's Linear-1 and Linear-2 tiles)
+  const long long max_slots = (max_tasks + kUnit - 1) / kUnit * kUnit + 2ll * kUnit * c->E;
+  L->max_slots = (int32_t)max_slots;
+  L->group_tasks = off;
+  off = align_up(off + (size_t)max_slots * 16, 256);
   L->total_bytes = off;
   return MOE_OK;
 }
@@ -188,8 +192,8 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.mb_ready = at<int32_t>(ws, L.mblk_ready);
   a.tasks = at<int32_t>(ws, L.tasks);
   a.unit_start = at<int32_t>(ws, L.unit_start);
-  a.unit_taken = at<int32_t>(ws, L.unit_taken);
   a.group_units = at<int32_t>(ws, L.group_units);
+  a.gtasks = at<int32_t>(ws, L.group_tasks);
   a.max_units = L.max_tasks;
   a.T = cfg->T;
   a.E = cfg->E;
@@ -246,10 +250,7 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_
   g.yd = yd;
   g.hdr = at<int32_t>(ws, L.header);
   g.tasks = at<int32_t>(ws, L.tasks);
-  g.unit_start = at<int32_t>(ws, L.unit_start);
-  g.unit_taken = at<int32_t>(ws, L.unit_taken);
-  g.group_units = at<int32_t>(ws, L.group_units);
-  g.max_units = L.max_tasks;
+  g.gtasks = at<int32_t>(ws, L.group_tasks);
   g.ngroups = 1;  // the launcher picks the group count from the grid it launches
   g.mb_expert = at<int32_t>(ws, L.mblk_expert);
   g.mb_row0 = at<int32_t>(ws, L.mblk_row0);
@@ -261,6 +262,7 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_
   g.E = cfg->E;
   g.n1 = L.n1_tiles;
   g.max_tasks = L.max_tasks;
+  g.max_slots = L.max_slots;
   g.max_mblk = L.max_mblk;
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;

@@ -6,8 +6,8 @@
 // and Section 4.2 reorders independent Linear-1 / Linear-2 tiles across waves. Here:
 //
 //  * A workgroup (8 wavefronts for 256-row tiles, 4 for smaller ones) takes the next tile of
-//    its XCD group's part of the list (unit cursor + per-unit counter), so each group's tiles
-//    start in list order whatever the grid size.
+//    its XCD group's part of the list (one atomic on the group's cursor, then the tile's
+//    record), so each group's tiles start in list order whatever the grid size.
 //  * Linear-1 tile (expert e, m-block, n-tile): 128 gate rows + the matching 128 up rows of
 //    W1[e] against up to tile_m dispatched rows; the epilogue forms
 //    A = bf16(silu(gate) * up) for 128 columns and releases the m-block's ready counter.
@@ -32,6 +32,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 
@@ -94,10 +95,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  // The task word and the exit flag live at the start of LDS stage 1: that stage is first
-  // written only after a barrier that every wave passes after reading the task word.
+  // The tile record and the exit flag live at the start of LDS stage 1: that stage is first
+  // written only after a barrier that every wave passes after reading the record.
   int* const s_task = reinterpret_cast<int*>(&lds[STAGE]);
-  int* const s_last = s_task + 1;
+  int* const s_last = s_task + 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % WN, wm = wave / WN;
@@ -111,59 +112,58 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   const __amdgpu_buffer_rsrc_t r_act = make_rsrc(p.act, act_bytes);
 
   // tile source: one shared cursor over the list, or (with kGroups groups) this workgroup's
-  // group takes its own units (in list order) one after the other, each unit's tiles in
-  // order, then the other groups' units in turn. Each group walks the list in order, so every
-  // tile a Linear-2 tile waits for is taken before it by a workgroup that never waits on a
-  // later tile.
+  // group list of tile records first, then the other groups' lists in turn. Each group walks
+  // its records in list order, so every tile a Linear-2 tile waits for is taken before it by a
+  // workgroup that never waits on a later tile. A claim is one atomic on the group's cursor
+  // (the list bounds load alongside it) and one 16-byte record load.
   const int my_group = (int)(blockIdx.x % (unsigned)p.ngroups);
-  int scan_group = 0;  // thread 0 only: groups visited so far
+  int scan_group = 0;  // thread 0 only: groups whose lists are used up
   for (;;) {
     if (tid == 0) {
-      int task = kNoTask;
-      const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
+      i32x4 rec = {kNoTask, -1, 0, 0};  // task word, expert, first row, rows
       if (p.ngroups == 1) {
+        const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
         const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
-        if (t < ntasks) task = p.tasks[t];
+        if (t >= 0 && t < ntasks) {
+          rec[0] = p.tasks[t];
+          const int mb = (rec[0] >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
+          if (mb < p.max_mblk) {  // the m-block record is read only for an index inside the table
+            rec[1] = p.mb_expert[mb];
+            rec[2] = p.mb_row0[mb];
+            rec[3] = p.mb_rows[mb];
+          }
+        }
       } else {
-        const int nunits = min(p.hdr[HDR_NUNITS], p.max_units);
         while (scan_group < p.ngroups) {
           const int g = (my_group + scan_group) % p.ngroups;
-          const int j = __hip_atomic_load(&p.hdr[HDR_GROUP_CURSOR + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const int g0 = p.hdr[HDR_GROUP_OFF + g], g1 = min(p.hdr[HDR_GROUP_OFF + g + 1], nunits);
-          if (g0 < 0 || g0 + j >= g1) {
-            ++scan_group;
+          const int i = atomicAdd(&p.hdr[HDR_GROUP_CURSOR + g], 1);
+          const int lo = max(p.hdr[HDR_GTASK_OFF + g], 0), hi = min(p.hdr[HDR_GTASK_OFF + g + 1], p.max_slots);
+          if (i >= 0 && i < hi - lo) {
+            rec = *reinterpret_cast<const i32x4*>(p.gtasks + 4 * (size_t)(lo + i));
+            if (rec[0] != kNopTask) break;
+            rec = i32x4{kNoTask, -1, 0, 0};  // a spare slot: claim again
             continue;
           }
-          const int u = p.group_units[g0 + j];
-          if ((unsigned)u >= (unsigned)nunits) {  // a plan this workspace could not have produced
-            atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
-            break;
-          }
-          const int lo = p.unit_start[u], hi = min(p.unit_start[u + 1], ntasks);
-          const int t = atomicAdd(&p.unit_taken[u], 1);
-          if (lo >= 0 && lo + t < hi) {
-            task = p.tasks[lo + t];
-            break;
-          }
-          atomicCAS(&p.hdr[HDR_GROUP_CURSOR + g], j, j + 1);  // unit used up: move the group on
+          ++scan_group;  // this group's list is used up
         }
       }
-      *s_task = task;
+      s_task[0] = rec[0];
+      s_task[1] = rec[1];
+      s_task[2] = rec[2];
+      s_task[3] = rec[3];
     }
     __syncthreads();
     // the task and its m-block record are the same for the whole workgroup: keep them scalar
-    const int task = __builtin_amdgcn_readfirstlane(*s_task);
+    const int task = __builtin_amdgcn_readfirstlane(s_task[0]);
     if (task == kNoTask) break;
     const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
     const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
     const int nt = task & kTaskNtMask;
-    // the m-block record is read only for an index inside the table
-    const bool mb_ok = mb < p.max_mblk;
-    const int e = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_expert[mb]) : -1;
-    const int row0 = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_row0[mb]) : 0;
-    const int nrows = mb_ok ? __builtin_amdgcn_readfirstlane(p.mb_rows[mb]) : 0;
+    const int e = __builtin_amdgcn_readfirstlane(s_task[1]);
+    const int row0 = __builtin_amdgcn_readfirstlane(s_task[2]);
+    const int nrows = __builtin_amdgcn_readfirstlane(s_task[3]);
     // a plan this workspace could not have produced: skip the tile, report, never fault
-    if (!mb_ok || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
+    if (mb >= p.max_mblk || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
         nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1)) {
       if (tid == 0) atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
       __syncthreads();
@@ -404,8 +404,6 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   if (*s_last) {
     const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
     for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
-    const int nu = min(p.hdr[HDR_NUNITS], p.max_units);
-    for (int i = tid; i < nu; i += NT) p.unit_taken[i] = 0;
     if (tid == 0) {
       p.hdr[HDR_CURSOR] = 0;
       for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;

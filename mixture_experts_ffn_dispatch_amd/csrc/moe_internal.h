@@ -20,12 +20,13 @@ enum : int {
   HDR_N1 = 5,
   HDR_N2 = 6,
   HDR_DONE = 7,    // persistent workgroups that have exited (the last one resets the state)
-  HDR_GROUP_CURSOR = 8,   // [8, 16): units each locality group has finished
+  HDR_GROUP_CURSOR = 8,   // [8, 16): records of each locality group's tile list handed out
   HDR_NUNITS = 16,        // units in the unit table
   HDR_GROUP_OFF = 17,     // [17, 26): first entry of each group's unit list (9th = end)
   HDR_LEAD = 26,          // interleave lead the plan used (0 for the Expert-Wave order)
   HDR_PLAN_GRID = 27,     // GEMM grid size the plan assumed when it chose the lead
-  HDR_SLOTS = 32
+  HDR_GTASK_OFF = 32,     // [32, 41): first record of each group's tile list (9th = end)
+  HDR_SLOTS = 64
 };
 
 // Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, which is
@@ -34,6 +35,9 @@ enum : int {
 // kBlockN n-tiles of one expert). Linear-1 units are dealt round-robin to the groups in list
 // order, and so are Linear-2 units, so every group gets an even share of both kinds of work;
 // the workgroups that share an XCD's L2 work on tiles of one unit, which share operand rows.
+// Each group's units, in its order, are also written out as one flat list of tile records
+// (task word, expert, first row, rows), kUnit slots per unit, so a workgroup claims a tile
+// with one atomic on its group's cursor and one 16-byte load.
 constexpr int kGroups = 8;
 constexpr int kUnit = 32;
 constexpr int kBlockM = 4;
@@ -50,6 +54,10 @@ constexpr int kDefaultSpinLimit = 1 << 22;
 // "no more tiles": all ones. Never a real task because m-block 0x7FFFF is out of range
 // (the host rejects plans with 2^19 - 1 or more m-blocks).
 constexpr int32_t kNoTask = -1;
+// A spare slot of a group record list (units own kUnit slots each; a short unit leaves some
+// empty): Linear-1, m-block 0x7FFFF (out of range, as above), n-tile 0xFFE. Claiming one just
+// means claiming again.
+constexpr int32_t kNopTask = 0x7FFFFFFE;
 
 // Task word: bit 31 = Linear-2, bits 30..12 = m-block, bits 11..0 = n-tile.
 __host__ __device__ inline int32_t make_task(int l2, int mblk, int nt) {
@@ -72,8 +80,8 @@ struct PlanArgs {
   int32_t* mb_ready;
   int32_t* tasks;
   int32_t* unit_start;  // [max_units + 1]: list position of each unit's first tile
-  int32_t* unit_taken;  // [max_units]: tiles taken from each unit in the current forward
   int32_t* group_units; // [max_units]: each group's units in list order, groups one after another
+  int32_t* gtasks;      // [slots][4]: each group's tile records (kUnit slots per unit), groups one after another
   int max_units;
   int T, E, k, chunks, chunk_tokens;
   int cstride;   // row stride of chunk_counts: chunks rounded up to a multiple of 4 (16 B)
@@ -95,12 +103,9 @@ struct GemmArgs {
   uint16_t* act;
   uint16_t* yd;
   int32_t* hdr;
-  const int32_t* tasks;  // the tile list in schedule order
-  const int32_t* unit_start;
-  int32_t* unit_taken;
-  const int32_t* group_units;
-  int max_units;
-  int ngroups;  // 1: one shared cursor over the list; kGroups: each group takes its own units
+  const int32_t* tasks;   // the tile list in schedule order (one shared cursor when ngroups is 1)
+  const int32_t* gtasks;  // [slots][4]: each group's tile records (task, expert, row0, rows)
+  int ngroups;  // 1: one shared cursor over the list; kGroups: each group takes its own records
   const int32_t* mb_expert;
   const int32_t* mb_row0;
   const int32_t* mb_rows;
@@ -109,6 +114,7 @@ struct GemmArgs {
   int H, I, E;
   int n1;  // Linear-1 n-tiles per m-block (the dependency target)
   int max_tasks, max_mblk;  // capacity of the workspace arrays (guards against a stale plan)
+  int max_slots;            // capacity of the group record lists
   int spin_limit;
   int force_timeout;
 };

@@ -388,6 +388,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   //    when there are more m-blocks than the table holds). In a merged segment, Linear-1
   //    unit v goes right after Linear-2 unit ceil((v+1) * bu / au) (bu, au: unit counts), which
   //    spreads the Linear-1 units evenly and ends the segment with the last Linear-1 unit.
+  //    Each tile also writes its record into its group's record list, where every unit owns
+  //    kUnit consecutive slots (a short unit's spare slots hold no-op records): so a tile's slot
+  //    is (the unit's index in the groups' unit lists) * kUnit + its offset in the unit.
   for (int ph = 0; ph < 2; ++ph) {
     const int n = ph ? a.n2 : a.n1;
     // tile u = (m-block u / n, n-tile u % n), stepped by kScanThreads without dividing again
@@ -440,15 +443,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
         other_before = s_p2[w - D] + c;
       }
       a.tasks[at] = make_task(ph, mb, nt);
+      // Units of each phase are dealt round-robin to the groups in list order: this unit is
+      // number pidx of its phase, so it goes to group pidx % G; its place in that group's list
+      // counts the group's earlier units of both phases.
+      const int pidx = (ph ? s_p2[w] : s_p1[w]) + ur;
+      const int g = pidx % kGroups;
+      const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
+      const size_t slot0 = (size_t)(s_goff[g] + rank) * kUnit;
+      // the record: task word, expert, first dispatched row and rows of the m-block
+      const int cnt_e = s_off[e + 1] - s_off[e];
+      i32x4 rec;
+      rec[0] = make_task(ph, mb, nt);
+      rec[1] = e;
+      rec[2] = s_off[e] + ml * BM;
+      rec[3] = min(BM, cnt_e - ml * BM);
+      *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + o)) = rec;
       if (o == 0) {
         a.unit_start[unit] = (int)at;
-        // Units of each phase are dealt round-robin to the groups in list order: this unit is
-        // number pidx of its phase, so it goes to group pidx % G; its place in that group's list
-        // counts the group's earlier units of both phases.
-        const int pidx = (ph ? s_p2[w] : s_p1[w]) + ur;
-        const int g = pidx % kGroups;
-        const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
         a.group_units[s_goff[g] + rank] = unit;
+        const int size = min(kUnit, (ph ? s_b[w] : s_a[w]) - ur * kUnit);
+        for (int q = size; q < kUnit; ++q)  // a short unit's spare slots
+          *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + q)) = i32x4{kNopTask, -1, 0, 0};
       }
       mb += dmb;
       nt += dnt;
@@ -458,12 +473,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       }
     }
   }
-  if (tid == 0) a.unit_start[total_units] = total_mb * (a.n1 + a.n2);
-  for (int i = tid; i < total_units; i += kScanThreads) a.unit_taken[i] = 0;
+  const int total_tiles = total_mb * (a.n1 + a.n2);
+  if (tid == 0) a.unit_start[total_units] = total_tiles;
+  if (tid <= kGroups) a.hdr[HDR_GTASK_OFF + tid] = s_goff[tid] * kUnit;
   if (tid == 0) {
     a.hdr[HDR_ERROR] = 0;
     a.hdr[HDR_CURSOR] = 0;
-    a.hdr[HDR_NTASKS] = total_mb * (a.n1 + a.n2);
+    a.hdr[HDR_NTASKS] = total_tiles;
     a.hdr[HDR_NMBLK] = total_mb;
     a.hdr[HDR_TILE_M] = BM;
     a.hdr[HDR_N1] = a.n1;

@@ -136,7 +136,7 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     b = run(cfg, dev)
     tasks, starts, gunits, goff, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
-    hdr = b["ws"][:128].cpu().numpy().view(np.int32)
+    hdr = b["ws"][:256].cpu().numpy().view(np.int32)
     used_lead, grid = int(hdr[26]), int(hdr[27])
     if schedule == moe.MOE_SCHED_EXPERT_WAVE:
         assert used_lead == 0
@@ -159,6 +159,29 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     lists = model_groups(units)
     assert goff == [sum(len(x) for x in lists[:g]) for g in range(9)]
     assert gunits == [u for x in lists for u in x]
+    # each group's tile records: its units in its order, UNIT slots per unit holding the unit's
+    # tiles with the m-block's expert, first dispatched row and row count; spare slots no-op
+    ws = b["ws"].cpu().numpy()
+    gtoff = hdr[32:41].tolist()
+    assert gtoff == [UNIT * g for g in goff]
+    recs = ws[L["group_tasks"]:L["group_tasks"] + 16 * UNIT * len(gunits)].view(np.int32).reshape(-1, 4)
+    assert len(gunits) * UNIT <= L["max_slots"]
+    offsets = b["offsets"].cpu().numpy()
+    first_mb, nxt = [], 0
+    for e in range(shape.E):
+        first_mb.append(nxt)
+        nxt += -(-int(counts[e]) // L["tile_m"])
+    NOP = 0x7FFFFFFE
+    for slot, u in enumerate(gunits):
+        block = recs[slot * UNIT:(slot + 1) * UNIT]
+        tiles = units[u]
+        assert all(int(r[0]) == NOP for r in block[len(tiles):])
+        assert [tuple(t) for t in decode(block[:len(tiles), 0])] == tiles
+        for (ph, mb, nt), (_, e, row0, rows) in zip(tiles, block[:len(tiles)].tolist()):
+            assert first_mb[e] <= mb < first_mb[e] + -(-int(counts[e]) // L["tile_m"])
+            i = mb - first_mb[e]
+            assert row0 == offsets[e] + i * L["tile_m"]
+            assert rows == min(L["tile_m"], int(counts[e]) - i * L["tile_m"])
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
     seen = {}
     for ph, mb, _ in tasks:
