@@ -185,6 +185,20 @@ __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
   return base + x - v;
 }
 
+// Minimum of one int per thread over a 1024-thread workgroup (the same value on every thread).
+__device__ int block_min(int v, int* s_tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  if (lane == 0) s_tmp[wave] = v;
+  __syncthreads();
+  int w = lane < kScanThreads / 64 ? s_tmp[lane] : 0x7fffffff;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) w = min(w, __shfl_xor(w, off));
+  __syncthreads();  // s_tmp may be reused by the next call
+  return w;
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a) {
   __shared__ int s_tmp[32];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];  // expert offsets
@@ -301,20 +315,46 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   __syncthreads();
   // Lead 0 picks D from the tile counts. A Linear-2 tile of wave i must not be taken before
   // the last Linear-1 tile of wave i has finished. With `grid` tiles in flight, list
-  // positions are taken at about grid per mean tile duration, so that takes about
-  // grid * t1 / t_mean positions (t1, t2: Linear-1 / Linear-2 tile durations, proportional
-  // to their K = H and I). Each lead wave beyond the first puts about one wave of tiles,
-  // (A + B) / nw, between them (A, B: Linear-1 / Linear-2 tiles in all waves). Hence
-  //   D = 1 + ceil(grid * H * nw / (A * H + B * I)),  clamped to [1, nw].
+  // positions are taken at about grid per mean tile duration, so a Linear-1 tile finishes
+  // about grid * t1 / t_mean positions after it was taken (t1, t_mean: Linear-1 and mean
+  // tile durations, proportional to K = H for Linear-1 and I for Linear-2). In the interleaved
+  // list the last Linear-1 tile of wave i ends segment i - D (or the lead prefix) and Linear-2
+  // of wave i starts segment i, so with a_j, b_j the Linear-1 / Linear-2 tiles of wave j and
+  // PA, PB their prefix sums the tiles between them number
+  //   dist_i(D) = PB[i] - PB[max(0, i - D + 1)] + PA[min(i + D, nw)] - PA[min(i + 1, nw)].
+  // D is the smallest lead with dist_i(D) * (A H + B I) >= grid * H * (A + B) for every wave
+  // with Linear-2 tiles (A, B: all Linear-1 / Linear-2 tiles), else nw. The prefix sums use
+  // s_p1 / s_p2, which are filled only after the lead is known.
   int D = a.lead;
   {
     int A, B;
-    block_exclusive_scan(aw, s_tmp, A);
-    block_exclusive_scan(bw, s_tmp, B);
+    const int pa = block_exclusive_scan(aw, s_tmp, A);
+    const int pb = block_exclusive_scan(bw, s_tmp, B);
     if (interleaved && D == 0) {
+      if (tid < nw) {
+        s_p1[tid] = pa;
+        s_p2[tid] = pb;
+      }
+      if (tid == 0) {
+        s_p1[nw] = A;
+        s_p2[nw] = B;
+      }
+      __syncthreads();
       const long long den = (long long)A * a.H + (long long)B * a.I;
-      const long long num = (long long)a.grid * a.H * nw;
-      D = den > 0 ? 1 + (int)min((num + den - 1) / den, (long long)nw) : 1;
+      const long long need = (long long)a.grid * a.H * (A + B);
+      int cand = nw;  // thread t tests lead t + 1
+      if (tid < nw) {
+        const int Dc = tid + 1;
+        bool ok = true;
+        for (int i = 0; i < nw && ok; ++i) {
+          if (s_b[i] == 0) continue;
+          const long long dist = (long long)s_p2[i] - s_p2[max(0, i - Dc + 1)] + s_p1[min(i + Dc, nw)] -
+                                 s_p1[min(i + 1, nw)];
+          ok = dist * den >= need;
+        }
+        if (ok) cand = Dc;
+      }
+      D = block_min(cand, s_tmp);
     }
     D = min(max(D, 1), max(nw, 1));
   }

@@ -115,15 +115,37 @@ def long_workload():
 
 
 def auto_lead(counts, tile_m, n1, n2, W_, H, I, grid):
-    """The lead moe_plan picks for lead_waves = 0: D = 1 + ceil(G*H*nw / (A*H + B*I)) over nw
-    waves with A Linear-1 and B Linear-2 tiles and G persistent workgroups, in [1, nw]."""
+    """The lead moe_plan picks for lead_waves = 0: the smallest D at which, for every wave i
+    with Linear-2 tiles, the tiles between the last Linear-1 tile of wave i and its first
+    Linear-2 tile (in the interleaved list) cover G * t1 / t_mean positions (durations
+    proportional to K = H, I), else nw. Counted directly on the model's list."""
     E = len(counts)
     nw = -(-E // W_)
-    mblocks = sum(-(-int(c) // tile_m) for c in counts)
-    A, B = mblocks * n1, mblocks * n2
+    mb = [-(-int(c) // tile_m) for c in counts]
+    a = [sum(mb[w * W_:(w + 1) * W_]) * n1 for w in range(nw)]
+    b = [sum(mb[w * W_:(w + 1) * W_]) * n2 for w in range(nw)]
+    A, B = sum(a), sum(b)
+    need = grid * H * (A + B)
     den = A * H + B * I
-    D = 1 + min(-(-(grid * H * nw) // den), nw) if den > 0 else 1
-    return min(max(D, 1), max(nw, 1))
+    for D in range(1, nw + 1):
+        seq = []  # (phase, wave) per tile in the interleaved list, tiles merged as whole runs
+        seq += [(0, w) for w in range(min(D, nw)) for _ in range(a[w])]
+        for i in range(nw):
+            seq += [(1, i)] * b[i]
+            if i + D < nw:
+                seq += [(0, i + D)] * a[i + D]
+        ok = True
+        for i in range(nw):
+            if b[i] == 0:
+                continue
+            last_l1 = max(p for p, t in enumerate(seq) if t == (0, i)) if a[i] else -1
+            first_l2 = min(p for p, t in enumerate(seq) if t == (1, i))
+            if (first_l2 - last_l1 - 1) * den < need:
+                ok = False
+                break
+        if ok:
+            return D
+    return max(nw, 1)
 
 
 @pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9), (1, 0)])
