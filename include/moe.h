@@ -67,11 +67,13 @@ enum {
 
 /* Lead chosen by moe_plan when lead_waves is 0 (interleaved order): a Linear-2 tile of wave w
    should be taken only after the last Linear-1 tile of wave w has finished. With G persistent
-   workgroups, list positions are taken at about G per mean tile duration, and each lead wave
-   beyond the first places about one wave of tiles between the two. Tile durations scale with
-   their K (H for Linear-1, I for Linear-2), so with A Linear-1 and B Linear-2 tiles over nw
-   waves:  D = 1 + ceil(G * H * nw / (A * H + B * I)), clamped to [1, nw]. The lead only
-   reorders tiles; results do not depend on it. */
+   workgroups, list positions are taken at about G per mean tile duration; tile durations scale
+   with their K (H for Linear-1, I for Linear-2). With a_j, b_j the Linear-1 / Linear-2 tiles of
+   wave j, A, B their totals and PA, PB their prefix sums, the tiles between the last Linear-1
+   tile of wave i and its first Linear-2 tile number
+     dist_i(D) = PB[i] - PB[max(0, i-D+1)] + PA[min(i+D, nw)] - PA[min(i+1, nw)],
+   and D is the smallest lead with dist_i(D) * (A*H + B*I) >= G * H * (A + B) for every wave
+   with Linear-2 tiles, else nw. The lead only reorders tiles; results do not depend on it. */
 
 /* Limits of this implementation (violations return MOE_ERR_UNSUPPORTED). */
 #define MOE_MAX_EXPERTS 1024 /* E                                        */
