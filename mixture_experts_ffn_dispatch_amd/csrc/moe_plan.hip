@@ -624,42 +624,85 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
          ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
+// Combine: a wavefront per token. Slot j's row and weight are held by lane j (k <= 64) and
+// broadcast with readlane; each lane takes two 16-byte chunks of the row per step and issues
+// the loads of up to KB slots before any is accumulated, so their latencies overlap. Every Yd
+// row is read exactly once, so the loads are non-temporal. The sum runs over j in ascending
+// order for every element.
+template <int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const float* w,
                                                       const uint16_t* yd, uint16_t* out, int T,
                                                       int H, int k, int R) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cpr = H / 8;
   for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
-    const int32_t* pt = pos + (size_t)t * k;
-    const float* wt = w + (size_t)t * k;
-    for (int c = lane; c < cpr; c += 64) {
-      float acc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 4
-      for (int j = 0; j < k; ++j) {  // fixed ascending order
-        int r = pt[j];
-        float wj = wt[j];
-        if ((unsigned)r >= (unsigned)R) {  // never for a plan written by moe_plan
-          r = 0;
-          wj = 0.f;
-        }
-        const u32x4 v = reinterpret_cast<const u32x4*>(yd + (size_t)r * H)[c];
-        acc[0] = fmaf(wj, bf16_lo(v.x), acc[0]);
-        acc[1] = fmaf(wj, bf16_hi(v.x), acc[1]);
-        acc[2] = fmaf(wj, bf16_lo(v.y), acc[2]);
-        acc[3] = fmaf(wj, bf16_hi(v.y), acc[3]);
-        acc[4] = fmaf(wj, bf16_lo(v.z), acc[4]);
-        acc[5] = fmaf(wj, bf16_hi(v.z), acc[5]);
-        acc[6] = fmaf(wj, bf16_lo(v.w), acc[6]);
-        acc[7] = fmaf(wj, bf16_hi(v.w), acc[7]);
+    int rv = 0;
+    float wv = 0.f;
+    if (lane < k) {
+      rv = pos[(size_t)t * k + lane];
+      wv = w[(size_t)t * k + lane];
+      if ((unsigned)rv >= (unsigned)R) {  // never for a plan written by moe_plan
+        rv = 0;
+        wv = 0.f;
       }
+    }
+    for (int c = lane; c < cpr; c += 128) {
+      const bool two = c + 64 < cpr;
+      float a0[8], a1[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.f;
+      for (int j0 = 0; j0 < k; j0 += KB) {
+        u32x4 v0[KB], v1[KB];
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj) {
+          if (j0 + jj < k) {
+            const int r = __builtin_amdgcn_readlane(rv, j0 + jj);
+            const u32x4* src = reinterpret_cast<const u32x4*>(yd + (size_t)r * H);
+            v0[jj] = __builtin_nontemporal_load(src + c);
+            if (two) v1[jj] = __builtin_nontemporal_load(src + c + 64);
+          }
+        }
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj) {
+          if (j0 + jj < k) {
+            const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wv), j0 + jj));
+            const u32x4 x = v0[jj];
+            a0[0] = fmaf(wj, bf16_lo(x.x), a0[0]);
+            a0[1] = fmaf(wj, bf16_hi(x.x), a0[1]);
+            a0[2] = fmaf(wj, bf16_lo(x.y), a0[2]);
+            a0[3] = fmaf(wj, bf16_hi(x.y), a0[3]);
+            a0[4] = fmaf(wj, bf16_lo(x.z), a0[4]);
+            a0[5] = fmaf(wj, bf16_hi(x.z), a0[5]);
+            a0[6] = fmaf(wj, bf16_lo(x.w), a0[6]);
+            a0[7] = fmaf(wj, bf16_hi(x.w), a0[7]);
+            if (two) {
+              const u32x4 y = v1[jj];
+              a1[0] = fmaf(wj, bf16_lo(y.x), a1[0]);
+              a1[1] = fmaf(wj, bf16_hi(y.x), a1[1]);
+              a1[2] = fmaf(wj, bf16_lo(y.y), a1[2]);
+              a1[3] = fmaf(wj, bf16_hi(y.y), a1[3]);
+              a1[4] = fmaf(wj, bf16_lo(y.z), a1[4]);
+              a1[5] = fmaf(wj, bf16_hi(y.z), a1[5]);
+              a1[6] = fmaf(wj, bf16_lo(y.w), a1[6]);
+              a1[7] = fmaf(wj, bf16_hi(y.w), a1[7]);
+            }
+          }
+        }
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(out + (size_t)t * H);
       u32x4 o;
-      o.x = pack_bf16(acc[0], acc[1]);
-      o.y = pack_bf16(acc[2], acc[3]);
-      o.z = pack_bf16(acc[4], acc[5]);
-      o.w = pack_bf16(acc[6], acc[7]);
-      reinterpret_cast<u32x4*>(out + (size_t)t * H)[c] = o;
+      o.x = pack_bf16(a0[0], a0[1]);
+      o.y = pack_bf16(a0[2], a0[3]);
+      o.z = pack_bf16(a0[4], a0[5]);
+      o.w = pack_bf16(a0[6], a0[7]);
+      dst[c] = o;
+      if (two) {
+        o.x = pack_bf16(a1[0], a1[1]);
+        o.y = pack_bf16(a1[2], a1[3]);
+        o.z = pack_bf16(a1[4], a1[5]);
+        o.w = pack_bf16(a1[6], a1[7]);
+        dst[c + 64] = o;
+      }
     }
   }
 }
@@ -705,7 +748,7 @@ hipError_t launch_dispatch(const int32_t* pos, const uint16_t* x, uint16_t* xd, 
 
 hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
                           int H, int k, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, w, yd, out, T,
+  hipLaunchKernelGGL(combine_kernel<8>, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, w, yd, out, T,
                      H, k, T * k);
   return hipGetLastError();
 }
