@@ -23,14 +23,51 @@
 namespace moe {
 namespace {
 
-__device__ inline bool ranks_before(float av, int ae, float bv, int be) {
-  // (logit descending, expert id ascending); -0 == +0 as IEEE comparison says
-  return av > bv || (av == bv && ae < be);
+// Order-preserving key of a logit: a larger float gives a larger key and -0, +0 give the same
+// key (IEEE comparison), so equal keys are equal logits. Every key of a logit is above 0,
+// which marks a slot that is taken or holds no expert. NaN is not a valid logit and is read
+// as -inf, so selection stays in range.
+__device__ inline unsigned logit_key(float x) {
+  unsigned u = __float_as_uint(x != x ? -INFINITY : x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ inline float key_logit(unsigned k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// max(x, x of the lane that the DPP pattern CTRL names); the patterns used here stay inside
+// a row of 16 lanes and name an active lane
+template <int CTRL>
+__device__ inline unsigned dpp_max(unsigned x) {
+  return max(x, (unsigned)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false));
+}
+
+// Maximum over every aligned group of S lanes, in each lane of the group (all lanes active).
+// Inside a row: quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors; the
+// rows of a 32- or 64-lane group are combined through readlane.
+template <int S>
+__device__ inline unsigned group_max(unsigned x) {
+  if (S >= 2) x = dpp_max<0xB1>(x);
+  if (S >= 4) x = dpp_max<0x4E>(x);
+  if (S >= 8) x = dpp_max<0x141>(x);
+  if (S >= 16) x = dpp_max<0x140>(x);
+  if (S >= 32) {
+    const unsigned r0 = __builtin_amdgcn_readlane(x, 0), r1 = __builtin_amdgcn_readlane(x, 16);
+    const unsigned r2 = __builtin_amdgcn_readlane(x, 32), r3 = __builtin_amdgcn_readlane(x, 48);
+    if (S == 32) x = (threadIdx.x & 32) ? max(r2, r3) : max(r0, r1);
+    else x = max(max(r0, r1), max(r2, r3));
+  }
+  return x;
 }
 
 constexpr int kPlanThreads = 1024;  // 16 wavefronts per block in route_hist and scatter
 constexpr int kPlanWaves = kPlanThreads / 64;
 
+// Top-k selection, one round per kept slot: the largest key among the candidates (descending
+// logit) is found with group_max, and of the lanes holding it the lowest expert id wins (ties
+// go to the lower id): in route_hist the first 64-expert block with a match, and in it the
+// lowest lane, found with a ballot.
 template <int R>  // logits held per lane: experts lane, lane + 64, ..., E <= 64 * R
 __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
   __shared__ int cnt[MOE_MAX_EXPERTS];
@@ -42,43 +79,38 @@ __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
   const int t_end = min(a.T, (chunk + 1) * a.chunk_tokens);
   for (int t = chunk * a.chunk_tokens + wave; t < t_end; t += kPlanWaves) {
     const float* row = a.logits + (size_t)t * a.E;
-    float v[R];
+    unsigned key[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int e = lane + 64 * r;
-      const float x = e < a.E ? row[e] : -INFINITY;
-      v[r] = (x != x) ? -INFINITY : x;  // NaN is not a valid logit; keep selection in range
+      key[r] = e < a.E ? logit_key(row[e]) : 0u;
     }
-    unsigned taken = 0;
     float my_v = 0.f, top = 0.f;
     int my_e = 0;
     for (int j = 0; j < a.k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+      unsigned lm = 0u;
+#pragma unroll
+      for (int r = 0; r < R; ++r) lm = max(lm, key[r]);
+      const unsigned m = group_max<64>(lm);  // > 0: k <= E leaves a candidate every round
+      int be = -1;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int e = lane + 64 * r;
-        if (e < a.E && !((taken >> r) & 1u) && ranks_before(v[r], e, bv, be)) {
-          bv = v[r];
-          be = e;
+        const unsigned long long b = __ballot(key[r] == m);
+        if (b) {
+          be = 64 * r + __ffsll((long long)b) - 1;
+          break;
         }
       }
+      if (lane == (be & 63)) {
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (ranks_before(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
+        for (int r = 0; r < R; ++r)
+          if (r == (be >> 6)) key[r] = 0u;
       }
-      // every lane now holds the same winner (a strict total order has one maximum)
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
       if (lane == j) {
-        my_v = bv;
+        my_v = key_logit(m);
         my_e = be;
       }
-      if (j == 0) top = bv;
+      if (j == 0) top = key_logit(m);
     }
     // softmax restricted to the kept logits; the full denominator cancels
     const float ex = lane < a.k ? expf(my_v - top) : 0.f;
@@ -98,7 +130,7 @@ __global__ __launch_bounds__(kPlanThreads) void route_hist_kernel(PlanArgs a) {
 
 // Routing for E <= 64: one token per S-lane segment of a wavefront (S = a power of two >= E),
 // so 64 / S tokens are routed at once. Same selection and weights as route_hist_kernel; the
-// butterflies stay inside a segment (XOR with offsets below S).
+// maxima and the weight sums stay inside a segment.
 template <int S>
 __global__ __launch_bounds__(kPlanThreads) void route_small_kernel(PlanArgs a) {
   __shared__ int cnt[MOE_MAX_EXPERTS];
@@ -112,30 +144,20 @@ __global__ __launch_bounds__(kPlanThreads) void route_small_kernel(PlanArgs a) {
   for (int t0 = chunk * a.chunk_tokens + wave * TPW; t0 < t_end; t0 += kPlanWaves * TPW) {
     const int t = t0 + seg;
     const bool live = t < t_end;
-    float x = live && sl < a.E ? a.logits[(size_t)t * a.E + sl] : -INFINITY;
-    x = (x != x) ? -INFINITY : x;  // NaN is not a valid logit; keep selection in range
-    bool taken = false;
+    unsigned key = live && sl < a.E ? logit_key(a.logits[(size_t)t * a.E + sl]) : 0u;
     float my_v = 0.f, top = 0.f;
     int my_e = 0;
     for (int j = 0; j < a.k; ++j) {
-      const bool cand = !taken && sl < a.E;
-      float bv = cand ? x : -INFINITY;
-      int be = cand ? sl : 0x7fffffff;
-#pragma unroll
-      for (int off = S / 2; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oe = __shfl_xor(be, off);
-        if (ranks_before(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (be == sl) taken = true;
+      const unsigned m = group_max<S>(key);  // 0 only in a segment past the chunk's end
+      unsigned long long b = __ballot(key == m && key != 0u);
+      if (S < 64) b = (b >> (seg * S)) & ((1ull << (S & 63)) - 1ull);
+      const int be = b ? __ffsll((long long)b) - 1 : -1;
+      if (be == sl) key = 0u;
       if (sl == j) {
-        my_v = bv;
+        my_v = key_logit(m);
         my_e = be;
       }
-      if (j == 0) top = bv;
+      if (j == 0) top = key_logit(m);
     }
     const float ex = sl < a.k ? expf(my_v - top) : 0.f;
     float sum = ex;

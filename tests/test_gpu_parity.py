@@ -125,15 +125,34 @@ def test_top1_single_expert_matches_dense_ffn():
     assert_close_rel(g["out"], R.f64_to_bf16_bits(dense["y"]), what="E=1 top-1 vs dense FFN")
 
 
-def test_routing_ties_and_signed_zero():
-    # equal logits and -0/+0 must pick the lower expert id first, exactly like the oracle
-    T, E, k = 128, 8, 3
+def tie_logits(T, E, k):
+    """Logits full of ties: equal values, -0 against +0, ties between experts e and e + 64
+    (different 64-expert blocks of one lane), and rows where fewer than k logits are finite so
+    that -inf logits are kept (lower ids first, weight 0)."""
     lg = np.zeros((T, E), np.float32)
     lg[1::2] = -0.0
-    lg[::3, 5] = 1.0
-    lg[::5, 2] = -0.0
+    lg[::3, 5 % E] = 1.0
+    lg[::5, 2 % E] = -0.0
     lg[::7] = np.float32(0.5)
+    if E > 64:
+        lg[::4, 3] = 2.0
+        lg[::4, 67] = 2.0
+        lg[1::4, E - 1] = 3.0
+        lg[1::4, E - 65] = 3.0
+        lg[3::8, 64:] = 4.0  # the lower block's ids lose to the higher block's larger logits
+    lg[2::9] = -np.inf
+    lg[2::9, : max(1, k // 2)] = np.float32(-1.0)
+    return lg
+
+
+@pytest.mark.parametrize("E,k", [(8, 3), (16, 5), (32, 8), (48, 7), (64, 6), (100, 8), (130, 5), (300, 12)])
+def test_routing_ties_and_signed_zero(E, k):
+    # equal logits and -0/+0 must pick the lower expert id first, exactly like the oracle; the
+    # shapes cover every route kernel (8- to 64-lane segments, 2 to 5 experts per lane)
+    T = 128
+    lg = tie_logits(T, E, k)
     s = W.shape(T=T, H=64, I=64, E=E, k=k, seed=23)
+    note(f"routing ties E={E} k={k}")
     d = W.generate(s, parts=("x", "w1", "w2"))
     d["logits"] = lg
     o = R.moe_layer(d["x"], lg, d["w1"], d["w2"], k)
