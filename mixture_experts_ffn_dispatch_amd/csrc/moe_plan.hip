@@ -180,43 +180,52 @@ constexpr int kMbExpertLds = 8192;  // m-blocks whose expert the tile placement 
 
 __device__ inline int units_of(int tiles) { return (tiles + kUnit - 1) / kUnit; }
 
+// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active), in DPP: row
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then lane 15 of rows 0 and 2 added into
+// rows 1 and 3 (row_bcast15) and lane 31 into rows 2 and 3 (row_bcast31). Lanes whose source
+// lies outside the row, or rows outside the row mask, add 0.
+__device__ inline int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);
+  return x;
+}
+
 // Exclusive scan of one int per thread over a 1024-thread workgroup; `total` gets the sum.
+// Every wavefront scans the 16 wavefront totals itself, so one barrier publishes them.
 __device__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const int x = wave_inclusive_scan(v);
   if (lane == 63) s_tmp[wave] = x;
   __syncthreads();
-  if (wave == 0) {
-    int w = lane < kScanThreads / 64 ? s_tmp[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(w, off);
-      if (lane >= off) w += y;
-    }
-    if (lane < kScanThreads / 64) s_tmp[lane] = w;
-  }
-  __syncthreads();
-  const int base = wave ? s_tmp[wave - 1] : 0;
-  total = s_tmp[kScanThreads / 64 - 1];
+  const int w = wave_inclusive_scan(lane < kScanThreads / 64 ? s_tmp[lane] : 0);
+  const int base = wave ? __builtin_amdgcn_readlane(w, wave - 1) : 0;
+  total = __builtin_amdgcn_readlane(w, kScanThreads / 64 - 1);
   __syncthreads();  // s_tmp may be reused by the next call
   return base + x - v;
+}
+
+// Minimum over each wavefront (all lanes active): the mirror patterns of group_max, then the
+// four row minima through readlane.
+__device__ inline int wave_min(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false));
+  x = min(x, __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false));
+  return min(min(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             min(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // Minimum of one int per thread over a 1024-thread workgroup (the same value on every thread).
 __device__ int block_min(int v, int* s_tmp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+  v = wave_min(v);
   if (lane == 0) s_tmp[wave] = v;
   __syncthreads();
-  int w = lane < kScanThreads / 64 ? s_tmp[lane] : 0x7fffffff;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) w = min(w, __shfl_xor(w, off));
+  const int w = wave_min(lane < kScanThreads / 64 ? s_tmp[lane] : 0x7fffffff);
   __syncthreads();  // s_tmp may be reused by the next call
   return w;
 }
@@ -272,12 +281,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
         const int e = wave + NW * (sg / segs_row), c0 = (sg % segs_row) * SEG, i0 = c0 + lane * 4;
         if (c0 == 0) run = 0;
         const int sum = v[b][0] + v[b][1] + v[b][2] + v[b][3];
-        int x = sum;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const int y = __shfl_up(x, off);
-          if (lane >= off) x += y;
-        }
+        const int x = wave_inclusive_scan(sum);
         int r = run + x - sum;  // exclusive prefix of this lane's first entry
         i32x4 q;
 #pragma unroll
@@ -286,7 +290,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
           r += v[b][i];
         }
         if (i0 < a.cstride) *reinterpret_cast<i32x4*>(a.chunk_counts + (size_t)e * a.cstride + i0) = q;
-        run += __shfl(x, 63);
+        run += __builtin_amdgcn_readlane(x, 63);
         if (c0 + SEG >= a.chunks && lane == 0) s_cnt[e] = run;
       }
     }
@@ -555,9 +559,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   }
 }
 
-// Stable ranks of a run of slots inside their experts, 64 slots per step: lanes holding the
-// same expert are found with a ballot, ranked by lane order, and the run's running count
-// `run[e]` (LDS) advances by their number. With `emit`, rows are written out.
+// Stable ranks of a run of slots inside their experts, 64 slots per step: every lane reads
+// the run's running count `run[e]` (LDS) of its expert, lanes holding the same expert are
+// found with a ballot per distinct expert (the leader's expert broadcast by readlane) and
+// ranked by lane order, and the expert's last lane advances `run[e]` by their number. With
+// `emit`, rows are written out.
 template <bool emit>
 __device__ void rank_run(const PlanArgs& a, int f0, int f1, int* run) {
   const int lane = threadIdx.x & 63;
@@ -566,17 +572,21 @@ __device__ void rank_run(const PlanArgs& a, int f0, int f1, int* run) {
     const int f = s + lane;
     int e = f < f1 ? a.topk_ids[f] : -1;
     if ((unsigned)e >= (unsigned)a.E) e = -1;
+    const int base = e >= 0 ? run[e] : 0;
     unsigned long long remaining = __ballot(e >= 0);
-    int row = -1;
+    int rank = 0, cnt = 0;
     while (remaining) {
       const int leader = __ffsll((long long)remaining) - 1;
-      const int ev = __shfl(e, leader);
-      const unsigned long long m = __ballot(e == ev) & remaining;
-      const int base = run[ev];
-      if (e == ev) row = base + __popcll(m & ((1ull << lane) - 1ull));
-      if (lane == leader) run[ev] = base + __popcll(m);
+      const int ev = __builtin_amdgcn_readlane(e, leader);
+      const unsigned long long m = __ballot(e == ev);
+      if (e == ev) {
+        rank = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+        cnt = __popcll(m);
+      }
       remaining &= ~m;
     }
+    const int row = base + rank;
+    if (e >= 0 && rank == cnt - 1) run[e] = base + cnt;
     if (emit && e >= 0 && (unsigned)row < (unsigned)R) {
       a.perm[row] = f;
       a.pos[f] = row;
