@@ -77,6 +77,8 @@ SWEEP = [
     (96, 64, 128, 64, 8, 8, 32),
     (200, 512, 256, 33, 5, 4, 256),
     (513, 128, 192, 3, 3, 1, 0),
+    (300, 64, 64, 1024, 32, 128, 0),  # the largest E and k the ABI accepts
+    (129, 128, 64, 1000, 17, 125, 32),
 ]
 
 
@@ -145,7 +147,8 @@ def tie_logits(T, E, k):
     return lg
 
 
-@pytest.mark.parametrize("E,k", [(8, 3), (16, 5), (32, 8), (48, 7), (64, 6), (100, 8), (130, 5), (300, 12)])
+@pytest.mark.parametrize("E,k", [(8, 3), (16, 5), (32, 8), (48, 7), (64, 6), (100, 8), (130, 5), (300, 12),
+                                 (1024, 32)])
 def test_routing_ties_and_signed_zero(E, k):
     # equal logits and -0/+0 must pick the lower expert id first, exactly like the oracle; the
     # shapes cover every route kernel (8- to 64-lane segments, 2 to 5 experts per lane)
