@@ -129,6 +129,8 @@ def main() -> int:
                     help="fused: Linear-1 gathers token rows itself (moe_forward_gather); separate: "
                          "moe_dispatch writes xd first")
     ap.add_argument("--num-workgroups", type=int, default=0)
+    ap.add_argument("--wide-tails", choices=["auto", "on", "off"], default="auto",
+                    help="wide last m-blocks: the library's choice, forced on, or off (comparison)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -168,7 +170,9 @@ def main() -> int:
     def make_cfg(name):
         return moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
                              schedule=sched[name], lead_waves=args.lead, tile_m=args.tile_m,
-                             num_workgroups=args.num_workgroups)
+                             num_workgroups=args.num_workgroups,
+                             flags={"auto": 0, "on": moe.MOE_FLAG_WIDE_TAILS,
+                                    "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails])
 
     stream = torch.cuda.current_stream()
 
@@ -278,6 +282,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "dispatch": args.dispatch, "lead_waves": args.lead,
+                   "wide_tails": args.wide_tails,
                    "lead_used": main_res["lead_used"],
                    "tile_m": main_res["layout"]["tile_m"], "seed": s.seed},
         "roofline": roof,

@@ -101,6 +101,17 @@ typedef struct moe_config {
    MOE_ERR_TIMEOUT recorded. Results are then undefined. Never set in production. */
 #define MOE_FLAG_FORCE_WAIT_TIMEOUT 0x1
 
+/* Wide last m-blocks. With 256-row tiles, moe_plan can run an m-block of at most 128 rows (an
+   expert's last, partial block) as tiles of 128 token rows by 512 weight rows: half as many
+   tiles as 256 x 256 ones, with no token rows of padding. moe_forward then launches the kernel
+   instance that runs them, which is about 1% slower on regular tiles. By default this is done
+   when the average expert fills at most two m-blocks (T * k <= 512 * E), where last blocks
+   are a large share of the tiles; MOE_FLAG_WIDE_TAILS forces it on and MOE_FLAG_NO_WIDE_TAILS
+   off (setting both is MOE_ERR_INVALID_ARG). Outputs are bit-identical either way: every
+   element keeps its K order. moe_plan and moe_forward must receive the same flags. */
+#define MOE_FLAG_NO_WIDE_TAILS 0x2
+#define MOE_FLAG_WIDE_TAILS 0x4
+
 /* Routing buffers, written by moe_plan and read by the later calls (device pointers). */
 typedef struct moe_routing {
   int32_t* topk_ids; /* [T, k]   expert of slot (t, j); j ascending = descending router logit  */

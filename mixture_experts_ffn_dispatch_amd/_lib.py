@@ -23,6 +23,8 @@ MOE_ERR_TIMEOUT = -5
 MOE_SCHED_EXPERT_WAVE = 0
 MOE_SCHED_INTERLEAVED = 1
 MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
+MOE_FLAG_NO_WIDE_TAILS = 0x2
+MOE_FLAG_WIDE_TAILS = 0x4
 
 
 class MoeError(RuntimeError):

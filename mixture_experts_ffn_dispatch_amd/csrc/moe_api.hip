@@ -27,7 +27,8 @@ moe_status check_config(const moe_config* c) {
   if (c->experts_per_wave < 1) return MOE_ERR_INVALID_ARG;
   if (c->schedule != MOE_SCHED_EXPERT_WAVE && c->schedule != MOE_SCHED_INTERLEAVED) return MOE_ERR_INVALID_ARG;
   if (c->lead_waves < 0 || c->num_workgroups < 0 || c->spin_limit < 0) return MOE_ERR_INVALID_ARG;
-  if (c->flags & ~MOE_FLAG_FORCE_WAIT_TIMEOUT) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
+  if ((c->flags & MOE_FLAG_NO_WIDE_TAILS) && (c->flags & MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (c->reserved[i] != 0) return MOE_ERR_INVALID_ARG;
   if (c->tile_m != 0 && c->tile_m != 32 && c->tile_m != 64 && c->tile_m != 128 && c->tile_m != 256)
@@ -209,7 +210,8 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.n2 = L.n2_tiles;
   a.H = cfg->H;
   a.I = cfg->I;
-  if (gemm_grid(L.tile_m, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
+  a.wide_tails = plan_wide_tails(cfg, L.tile_m) ? 1 : 0;
+  if (gemm_grid(L.tile_m, a.wide_tails != 0, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_scan_schedule(a, s) != hipSuccess) return MOE_ERR_HIP;
@@ -267,7 +269,7 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (launch_gemm(g, L.tile_m, cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm(g, L.tile_m, plan_wide_tails(cfg, L.tile_m), cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
 }
 }  // namespace

@@ -79,20 +79,28 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW>
+template <int BM, int WN, int WM, int MINW, bool WIDE>
 __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
   constexpr int FN = BN / WN / 32;  // 32x32 MFMA blocks per wave along weight rows
   constexpr int FM = BM / WM / 32;  // ... along token rows
-  constexpr int ROWS = BN + BM;     // LDS rows per stage: weights first, then tokens
-  constexpr int STAGE = ROWS * BK;  // bf16 elements per stage
   constexpr int NT = 64 * WN * WM;  // threads
   constexpr int RG = NT / 8;        // operand rows staged per thread-wide step (8 chunks a row)
-  constexpr int LD = ROWS / RG;     // 16-byte chunks each thread stages per K step
+  // Wide tiles (the WIDE instance of the 256-row variant): an m-block of at most BM / 2 rows is
+  // run as one tile of 2 BN weight rows by BM / 2 token rows, the wavefronts arranged
+  // 2 WN x WM / 2, so that every wavefront keeps its (BN / WN) x (BM / WM) block, its fragments
+  // and its MFMA chain. The capability costs about 1% on regular tiles, so the other instance
+  // leaves it out.
+  constexpr bool WIDE_OK = WIDE && BM == 256 && WN == 2 && WM == 4;
+  constexpr int ROWS = WIDE_OK ? 2 * BN + BM / 2 : BN + BM;  // LDS rows per stage (weights, then tokens)
+  constexpr int STAGE = ROWS * BK;  // bf16 elements per stage
+  constexpr int LD = ROWS / RG;     // 16-byte chunks a thread may stage per K step
+  constexpr int LDN = BN / RG;      // of them weight chunks of a regular tile
   static_assert(FN % 2 == 0 && FN >= 2 && FM >= 1, "tile shape");
   static_assert(BM % RG == 0 && BN % (2 * RG) == 0 && RG % 16 == 0, "staging groups");
   static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
+  static_assert(!WIDE_OK || (LD == LDN + BM / RG + 2 && (BM / 2) % RG == 0), "wide staging");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
   // The tile record and the exit flag live at the start of LDS stage 1: that stage is first
@@ -101,7 +109,6 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   int* const s_last = s_task + 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WN, wm = wave / WN;
   const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, LDS chunk slot
   const int lds_pchunk = lchunk ^ swz(lrow);    // swizzled chunk (rows RG apart swizzle alike)
   const int fr_row = lane & 31, fr_chunk = lane >> 5;
@@ -123,8 +130,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       i32x4 rec = {kNoTask, -1, 0, 0};  // task word, expert, first row, rows
       if (p.ngroups == 1) {
         const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
-        const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
-        if (t >= 0 && t < ntasks) {
+        for (;;) {
+          const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
+          if (t < 0 || t >= ntasks) break;
           rec[0] = p.tasks[t];
           const int mb = (rec[0] >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
           if (mb < p.max_mblk) {  // the m-block record is read only for an index inside the table
@@ -132,6 +140,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
             rec[2] = p.mb_row0[mb];
             rec[3] = p.mb_rows[mb];
           }
+          // the odd n-tiles of a wide m-block are covered by the even ones: claim again
+          if (!((rec[3] & kRowsWide) && (rec[0] & 1))) break;
+          rec = i32x4{kNoTask, -1, 0, 0};
         }
       } else {
         while (scan_group < p.ngroups) {
@@ -161,19 +172,29 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const int nt = task & kTaskNtMask;
     const int e = __builtin_amdgcn_readfirstlane(s_task[1]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_task[2]);
-    const int nrows = __builtin_amdgcn_readfirstlane(s_task[3]);
+    const int rows_word = __builtin_amdgcn_readfirstlane(s_task[3]);
+    const bool wide = WIDE_OK && (rows_word & kRowsWide) != 0;
+    const int nrows = rows_word & ~kRowsWide;
     // a plan this workspace could not have produced: skip the tile, report, never fault
     if (mb >= p.max_mblk || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
-        nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1)) {
+        nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1) || (rows_word & kRowsWide && !WIDE_OK) ||
+        (wide && (nrows > BM / 2 || (nt & 1)))) {
       if (tid == 0) atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_WORKSPACE);
       __syncthreads();
       continue;
     }
     const int K = l2 ? p.I : p.H;
 
+    // tile geometry: weight rows and token rows in LDS, and this wavefront's place in the grid
+    const int bn = wide ? 2 * BN : BN;
+    const int bm = wide ? BM / 2 : BM;
+    const int wn = wide ? wave % (2 * WN) : wave % WN;
+    const int wm = wide ? wave / (2 * WN) : wave / WN;
+
     if (l2) {
       if (tid == 0) {
-        const int need = p.n1 + p.force_timeout;
+        // every Linear-1 tile of the m-block releases once; a wide m-block has half as many
+        const int need = (wide ? (p.n1 + 1) / 2 : p.n1) + p.force_timeout;
         int spins = 0;
         while (__hip_atomic_load(&p.mb_ready[mb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
           if (++spins > p.spin_limit) {
@@ -226,7 +247,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const uint32_t up_off = l2 ? 0u : (uint32_t)p.I * rowb;  // Linear-1: up rows follow the gate rows
     auto chunk_soff = [&](int i) -> uint32_t {
       if (l2) return (uint32_t)i * RG * rowb;
-      return i < BN / (2 * RG) ? (uint32_t)i * RG * rowb : up_off + (uint32_t)(i - BN / (2 * RG)) * RG * rowb;
+      const int half = bn / (2 * RG);  // chunks of gate rows
+      return i < half ? (uint32_t)i * RG * rowb : up_off + (uint32_t)(i - half) * RG * rowb;
     };
 
     f32x16 acc[FN][FM];
@@ -243,7 +265,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     for (int f = 0; f < FN; ++f) {
       if (l2) wrow[f] = wn * (BN / WN) + f * 32;
       else
-        wrow[f] = (f < FN / 2) ? wn * (BN / 2 / WN) + f * 32 : BN / 2 + wn * (BN / 2 / WN) + (f - FN / 2) * 32;
+        wrow[f] = (f < FN / 2) ? wn * (BN / 2 / WN) + f * 32 : bn / 2 + wn * (BN / 2 / WN) + (f - FN / 2) * 32;
     }
 
     // Mainloop, software-pipelined by hand. Per K step of 64 (four MFMA k-steps of 16):
@@ -270,8 +292,16 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
 #pragma unroll
       for (int i = 0; i < LD; ++i) {
         uint16_t* dst = &lds[st * STAGE + (wave_u * 8 + RG * i) * BK];
-        if (i < BN / RG) load_lds16(r_w, dst, vw, chunk_soff(i) + (uint32_t)kt * BK * 2u);
-        else load_lds16(r_t, dst, vtok[i - BN / RG] | past, (uint32_t)kt * BK * 2u);
+        const uint32_t ks = (uint32_t)kt * BK * 2u;
+        if (i < LDN) {
+          load_lds16(r_w, dst, vw, chunk_soff(i) + ks);
+        } else if (!WIDE_OK || i < 2 * LDN) {
+          // token chunk i - LDN of a regular tile, or weight chunk i of a wide one
+          const bool wch = WIDE_OK && wide;
+          load_lds16(wch ? r_w : r_t, dst, wch ? vw : (vtok[i - LDN] | past), (wch ? chunk_soff(i) : 0u) + ks);
+        } else if (wide) {
+          load_lds16(r_t, dst, vtok[i - 2 * LDN] | past, ks);  // token chunks of a wide tile
+        }
       }
     };
     auto read_frags = [&](int st, int ks, int set) {
@@ -281,7 +311,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       for (int f = 0; f < FN; ++f) fa[set][f] = *reinterpret_cast<const bf16x8*>(base + (wrow[f] + fr_row) * BK + pc);
 #pragma unroll
       for (int m = 0; m < FM; ++m)
-        fb[set][m] = *reinterpret_cast<const bf16x8*>(base + (BN + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
+        fb[set][m] = *reinterpret_cast<const bf16x8*>(base + (bn + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
     };
     auto mfmas = [&](int set) {
 #pragma unroll
@@ -335,8 +365,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     // r mod (chunks per row). A lane holds, for output block (f, m), columns
     // 8g + 4*(lane>>5) + {0..3} of the weight fragment at token row lane & 31.
     {
-      const int OC = l2 ? BN : BN / 2;  // output columns of the tile
-      const int CPR = OC / 8;           // 16-byte chunks per row (32 or 16)
+      const int OC = l2 ? bn : bn / 2;  // output columns of the tile
+      const int CPR = OC / 8;           // 16-byte chunks per row (16, 32 or 64)
       uint8_t* const obuf = reinterpret_cast<uint8_t*>(lds);
       auto obuf_off = [&](int row, int chunk) -> int { return row * OC * 2 + ((chunk ^ (row & (CPR - 1))) << 4); };
 #pragma unroll
@@ -374,10 +404,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       // row segments; rows past the m-block and columns past the matrix are not stored
       const int ldim = l2 ? p.H : p.I;
       const int col0 = l2 ? nt * kTileN2 : nt * kTileN1;
-      const int c = tid % CPR, col = col0 + c * 8;
+      const int c = tid & (CPR - 1), col = col0 + c * 8;
       const __amdgpu_buffer_rsrc_t r_out = l2 ? r_yd : r_act;
       if (col < ldim) {  // ldim is a multiple of 64, so a chunk is wholly inside or outside
-        for (int r = tid / CPR; r < nrows && r < BM; r += NT / CPR) {
+        for (int r = tid / CPR; r < nrows && r < bm; r += NT / CPR) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + obuf_off(r, c));
           __builtin_amdgcn_raw_buffer_store_b128(v, r_out, (int)(((uint32_t)(row0 + r) * (uint32_t)ldim + (uint32_t)col) * 2u), 0, 0);
         }
@@ -412,9 +442,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   }
 }
 
-template <int BM, int WN, int WM, int MINW>
+template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t variant_grid(int num_workgroups, int* grid) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -430,12 +460,12 @@ hipError_t variant_grid(int num_workgroups, int* grid) {
   return hipSuccess;
 }
 
-template <int BM, int WN, int WM, int MINW>
+template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW>;
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE>;
   constexpr int NT = 64 * WN * WM;
   int grid = 0;
-  hipError_t err = variant_grid<BM, WN, WM, MINW>(num_workgroups, &grid);
+  hipError_t err = variant_grid<BM, WN, WM, MINW, WIDE>(num_workgroups, &grid);
   if (err != hipSuccess) return err;
   GemmArgs g = a;
   g.ngroups = grid >= kGroups ? kGroups : 1;
@@ -445,22 +475,26 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 
 }  // namespace
 
-hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& a, int tile_m, bool wide, int num_workgroups, hipStream_t s) {
   switch (tile_m) {
-    case 256: return launch_variant<256, 2, 4, 2>(a, num_workgroups, s);
-    case 128: return launch_variant<128, 2, 2, 1>(a, num_workgroups, s);
-    case 64: return launch_variant<64, 4, 1, 2>(a, num_workgroups, s);
-    case 32: return launch_variant<32, 4, 1, 2>(a, num_workgroups, s);
+    case 256:
+      return wide ? launch_variant<256, 2, 4, 2, true>(a, num_workgroups, s)
+                  : launch_variant<256, 2, 4, 2, false>(a, num_workgroups, s);
+    case 128: return launch_variant<128, 2, 2, 1, false>(a, num_workgroups, s);
+    case 64: return launch_variant<64, 4, 1, 2, false>(a, num_workgroups, s);
+    case 32: return launch_variant<32, 4, 1, 2, false>(a, num_workgroups, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid) {
+hipError_t gemm_grid(int tile_m, bool wide, int num_workgroups, int* grid) {
   switch (tile_m) {
-    case 256: return variant_grid<256, 2, 4, 2>(num_workgroups, grid);
-    case 128: return variant_grid<128, 2, 2, 1>(num_workgroups, grid);
-    case 64: return variant_grid<64, 4, 1, 2>(num_workgroups, grid);
-    case 32: return variant_grid<32, 4, 1, 2>(num_workgroups, grid);
+    case 256:
+      return wide ? variant_grid<256, 2, 4, 2, true>(num_workgroups, grid)
+                  : variant_grid<256, 2, 4, 2, false>(num_workgroups, grid);
+    case 128: return variant_grid<128, 2, 2, 1, false>(num_workgroups, grid);
+    case 64: return variant_grid<64, 4, 1, 2, false>(num_workgroups, grid);
+    case 32: return variant_grid<32, 4, 1, 2, false>(num_workgroups, grid);
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,6 +58,10 @@ constexpr int32_t kNoTask = -1;
 // empty): Linear-1, m-block 0x7FFFF (out of range, as above), n-tile 0xFFE. Claiming one just
 // means claiming again.
 constexpr int32_t kNopTask = 0x7FFFFFFE;
+// Bit of a record's (and the m-block table's) row count that marks a wide m-block: with
+// 256-row tiles, an m-block of at most 128 rows runs as tiles of 512 weight rows (two n-tiles,
+// the even one named in the task word) by 128 token rows; its odd n-tiles hold no-op records.
+constexpr int32_t kRowsWide = 1 << 30;
 
 // Task word: bit 31 = Linear-2, bits 30..12 = m-block, bits 11..0 = n-tile.
 __host__ __device__ inline int32_t make_task(int l2, int mblk, int nt) {
@@ -91,6 +95,7 @@ struct PlanArgs {
   int tile_m, n1, n2;
   int H, I;      // Linear-1 K = H, Linear-2 K = I (tile durations scale with them)
   int grid;      // persistent GEMM workgroups (tiles in flight)
+  int wide_tails;  // 1: m-blocks of at most tile_m / 2 rows become wide (256-row tiles only)
 };
 
 struct GemmArgs {
@@ -128,9 +133,19 @@ hipError_t launch_dispatch(const int32_t* pos, const uint16_t* x, uint16_t* xd, 
 hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
                           int H, int k, hipStream_t s);
 // Persistent grouped GEMM; grid = num_workgroups (0 = CUs x occupancy).
-hipError_t launch_gemm(const GemmArgs& a, int tile_m, int num_workgroups, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, int tile_m, bool wide, int num_workgroups, hipStream_t s);
 // The grid launch_gemm uses for this tile height and request (every workgroup resident at once).
-hipError_t gemm_grid(int tile_m, int num_workgroups, int* grid);
+hipError_t gemm_grid(int tile_m, bool wide, int num_workgroups, int* grid);
+
+// Whether moe_plan writes wide last m-blocks, and moe_forward launches the kernel instance that
+// runs them: only with 256-row tiles; MOE_FLAG_WIDE_TAILS / MOE_FLAG_NO_WIDE_TAILS force the
+// choice, else wide when the average expert fills at most two m-blocks (T * k <= 2 * 256 * E),
+// where last blocks are a large share of the tiles. Both calls derive it from the same config.
+inline bool plan_wide_tails(const moe_config* c, int tile_m) {
+  if (tile_m != 256 || (c->flags & MOE_FLAG_NO_WIDE_TAILS)) return false;
+  if (c->flags & MOE_FLAG_WIDE_TAILS) return true;
+  return (long long)c->T * c->k <= 2ll * 256 * c->E;
+}
 // Burst-Gap microbenchmark: `producers` workgroups, each storing `bytes` per burst into its own
 // `region` of buf, `periods` times, with a busy gap of `gap_ticks` real-time counter ticks.
 hipError_t launch_burst_gap(uint8_t* buf, size_t region, int producers, int bytes, int periods,

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     for (int i = 0; i < nmb; ++i) {
       a.mb_expert[mb0 + i] = tid;
       a.mb_row0[mb0 + i] = s_off[tid] + i * BM;
-      a.mb_rows[mb0 + i] = min(BM, cnt - i * BM);
+      const int rows = min(BM, cnt - i * BM);
+      a.mb_rows[mb0 + i] = rows | (a.wide_tails && 2 * rows <= BM ? kRowsWide : 0);
       if (mb0 + i < kMbExpertLds) s_mbe[mb0 + i] = (short)tid;
     }
   }
@@ -523,6 +524,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       rec[1] = e;
       rec[2] = s_off[e] + ml * BM;
       rec[3] = min(BM, cnt_e - ml * BM);
+      if (a.wide_tails && 2 * rec[3] <= BM) {  // a wide m-block: even n-tiles cover two
+        rec[3] |= kRowsWide;
+        if (nt & 1) rec = i32x4{kNopTask, -1, 0, 0};
+      }
       *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + o)) = rec;
       if (o == 0) {
         a.unit_start[unit] = (int)at;

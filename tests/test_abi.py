@@ -70,7 +70,8 @@ def test_auto_tile_height(T, k, E, tile):
     (dict(schedule=2), moe.MOE_ERR_INVALID_ARG),
     (dict(lead_waves=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(tile_m=48), moe.MOE_ERR_UNSUPPORTED),
-    (dict(flags=4), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=8), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=6), moe.MOE_ERR_INVALID_ARG),  # wide last m-blocks forced both on and off
     (dict(reserved=(0, 1, 0, 0)), moe.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=8192, k=8, E=64), moe.MOE_ERR_UNSUPPORTED),  # row buffers past 4 GiB
 ])

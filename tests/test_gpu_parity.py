@@ -77,6 +77,8 @@ SWEEP = [
     (96, 64, 128, 64, 8, 8, 32),
     (200, 512, 256, 33, 5, 4, 256),
     (513, 128, 192, 3, 3, 1, 0),
+    (150, 768, 320, 6, 2, 2, 256),  # 256-row tiles: wide last m-blocks, odd and partial n-tiles
+    (300, 192, 384, 3, 1, 1, 256),
     (300, 64, 64, 1024, 32, 128, 0),  # the largest E and k the ABI accepts
     (129, 128, 64, 1000, 17, 125, 32),
 ]

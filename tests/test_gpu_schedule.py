@@ -9,7 +9,7 @@ import torch
 
 import moe_workloads as W
 from oracle import moe_ref as R
-from tests.gpu_util import Device, fetch, make_cfg, note, run
+from tests.gpu_util import Device, assert_close_rel, fetch, make_cfg, note, run
 
 import mixture_experts_ffn_dispatch_amd as moe
 
@@ -149,12 +149,14 @@ def auto_lead(counts, tile_m, n1, n2, W_, H, I, grid):
 
 
 @pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9), (1, 0)])
-@pytest.mark.parametrize("tile_m", [32, 128])
+@pytest.mark.parametrize("tile_m", [32, 128, 256])
 @pytest.mark.parametrize("which", ["short", "long"])
 def test_task_list_matches_model(workload, long_workload, which, schedule, lead, tile_m):
     shape, dev = (SHAPE, workload[1]) if which == "short" else (LONG, long_workload)
-    cfg = make_cfg(shape, schedule=schedule, lead_waves=lead, tile_m=tile_m)
-    note(f"task list {which} schedule={schedule} lead={lead} tile_m={tile_m}")
+    # with 256-row tiles, force wide last m-blocks (the long shape would not choose them)
+    flags = moe.MOE_FLAG_WIDE_TAILS if tile_m == 256 else 0
+    cfg = make_cfg(shape, schedule=schedule, lead_waves=lead, tile_m=tile_m, flags=flags)
+    note(f"task list {which} schedule={schedule} lead={lead} tile_m={tile_m} flags={flags}")
     b = run(cfg, dev)
     tasks, starts, gunits, goff, L = read_tasks(cfg, b)
     counts = b["counts"].cpu().numpy()
@@ -193,17 +195,30 @@ def test_task_list_matches_model(workload, long_workload, which, schedule, lead,
     for e in range(shape.E):
         first_mb.append(nxt)
         nxt += -(-int(counts[e]) // L["tile_m"])
-    NOP = 0x7FFFFFFE
+    NOP, WIDE = 0x7FFFFFFE, 1 << 30
+    tm = L["tile_m"]
+    mb_expert = [e for e in range(shape.E) for _ in range(-(-int(counts[e]) // tm))]
+    n_wide = 0
     for slot, u in enumerate(gunits):
         block = recs[slot * UNIT:(slot + 1) * UNIT]
         tiles = units[u]
         assert all(int(r[0]) == NOP for r in block[len(tiles):])
-        assert [tuple(t) for t in decode(block[:len(tiles), 0])] == tiles
-        for (ph, mb, nt), (_, e, row0, rows) in zip(tiles, block[:len(tiles)].tolist()):
-            assert first_mb[e] <= mb < first_mb[e] + -(-int(counts[e]) // L["tile_m"])
+        for (ph, mb, nt), rec in zip(tiles, block[:len(tiles)].tolist()):
+            e = mb_expert[mb]
             i = mb - first_mb[e]
-            assert row0 == offsets[e] + i * L["tile_m"]
-            assert rows == min(L["tile_m"], int(counts[e]) - i * L["tile_m"])
+            expect_rows = min(tm, int(counts[e]) - i * tm)
+            # with 256-row tiles an m-block of at most 128 rows is wide: its even n-tiles cover
+            # two, its odd ones hold no-op records
+            wide = tm == 256 and 2 * expect_rows <= tm
+            if wide and nt % 2:
+                assert rec[0] == NOP
+                continue
+            n_wide += wide
+            assert tuple(decode(np.array([rec[0]]))[0]) == (ph, mb, nt)
+            assert rec[1] == e and rec[2] == offsets[e] + i * tm
+            assert rec[3] == expect_rows | (WIDE if wide else 0)
+    if tm == 256 and which == "long":
+        assert n_wide > 0  # five of its experts end in a block of at most 128 rows
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
     seen = {}
     for ph, mb, _ in tasks:
@@ -227,6 +242,67 @@ def test_all_orders_grids_and_tiles_byte_identical(workload):
         np.testing.assert_array_equal(g["perm"], o["perm"])
         if ref is None:
             ref = g
+            continue
+        for key in ("act", "yd", "out"):
+            assert np.array_equal(g[key], ref[key]), (v, key)
+
+
+# Wide last m-blocks: with 256-row tiles an m-block of at most 128 rows runs as tiles of 512
+# weight rows by 128 token rows. Shapes with some experts ending in such a block and others
+# not, even and odd (and partial) n-tile counts.
+WIDE_SHAPES = [
+    # counts about 1024: five experts end in a block of at most 128 rows; n1 = 4, n2 = 1; the
+    # default would not choose wide blocks here (T k > 512 E)
+    LONG,
+    # counts about 400: two experts end in a block of at most 128 rows; n1 = 3, n2 = 2; chosen
+    # by default (T k <= 512 E)
+    W.shape(T=1200, H=384, I=320, E=6, k=2, experts_per_wave=2, seed=44, x_std=1.0, w_std=0.05),
+]
+
+
+def wide_records(cfg, bufs):
+    """Number of tile records the plan marked wide (bit 30 of the row count)."""
+    L = moe.moe_workspace_layout(cfg)
+    hdr = bufs["ws"][:256].cpu().numpy().view(np.int32)
+    n = int(hdr[40])  # end of the last group's record list
+    recs = bufs["ws"][L["group_tasks"]:L["group_tasks"] + 16 * n].cpu().numpy().view(np.int32).reshape(-1, 4)
+    return int(((recs[:, 0] != 0x7FFFFFFE) & ((recs[:, 3] & (1 << 30)) != 0)).sum())
+
+
+@pytest.mark.parametrize("which", [0, 1])
+def test_wide_tail_tiles_byte_identical(which):
+    shape = WIDE_SHAPES[which]
+    d = W.generate(shape)
+    dev = Device(d)
+    o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], shape.k)
+    tails = o["counts"] % 256
+    assert ((tails > 0) & (tails <= 128)).any() and ((tails == 0) | (tails > 128)).any()
+    # regular tiles everywhere first, then wide ones on the shared cursor (grid 1) and on the
+    # group lists, in both orders, with rows from xd and gathered from x
+    NO, ON = moe.MOE_FLAG_NO_WIDE_TAILS, moe.MOE_FLAG_WIDE_TAILS
+    variants = [dict(flags=NO, schedule=1), dict(flags=ON, schedule=1), dict(flags=ON, schedule=0),
+                dict(flags=ON, schedule=0, num_workgroups=1), dict(flags=ON, schedule=1, num_workgroups=3),
+                dict(flags=ON, schedule=1, lead_waves=2, gather=True), dict(flags=ON, schedule=0, gather=True),
+                dict(flags=NO, schedule=0, num_workgroups=1, gather=True), dict(schedule=1)]
+    ref = None
+    for v in variants:
+        v = dict(v)
+        gather = v.pop("gather", False)
+        note(f"wide tails {shape.T}x{shape.E} variant {v} gather={gather}")
+        cfg = make_cfg(shape, tile_m=256, **v)
+        bufs = run(cfg, dev, gather=gather)
+        flags = v.get("flags", 0)
+        auto = shape.T * shape.k <= 512 * shape.E
+        if flags == ON or (flags == 0 and auto):
+            assert wide_records(cfg, bufs) > 0
+        else:
+            assert wide_records(cfg, bufs) == 0
+        g = fetch(bufs, keys=("act", "yd", "out", "perm"))
+        np.testing.assert_array_equal(g["perm"], o["perm"])
+        if ref is None:
+            ref = g
+            for key, what in (("act", "a"), ("yd", "yd"), ("out", "out")):
+                assert_close_rel(g[key], o[what], what=key)
             continue
         for key in ("act", "yd", "out"):
             assert np.array_equal(g[key], ref[key]), (v, key)
