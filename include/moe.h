@@ -105,7 +105,7 @@ typedef struct moe_config {
    expert's last, partial block) as tiles of 128 token rows by 512 weight rows: half as many
    tiles as 256 x 256 ones, with no token rows of padding. moe_forward then launches the kernel
    instance that runs them, which is about 1% slower on regular tiles. By default this is done
-   when the average expert fills at most two m-blocks (T * k <= 512 * E), where last blocks
+   when the average expert fills at most three m-blocks (T * k <= 768 * E), where last blocks
    are a large share of the tiles; MOE_FLAG_WIDE_TAILS forces it on and MOE_FLAG_NO_WIDE_TAILS
    off (setting both is MOE_ERR_INVALID_ARG). Outputs are bit-identical either way: every
    element keeps its K order. moe_plan and moe_forward must receive the same flags. */

@@ -139,12 +139,12 @@ hipError_t gemm_grid(int tile_m, bool wide, int num_workgroups, int* grid);
 
 // Whether moe_plan writes wide last m-blocks, and moe_forward launches the kernel instance that
 // runs them: only with 256-row tiles; MOE_FLAG_WIDE_TAILS / MOE_FLAG_NO_WIDE_TAILS force the
-// choice, else wide when the average expert fills at most two m-blocks (T * k <= 2 * 256 * E),
+// choice, else wide when the average expert fills at most three m-blocks (T * k <= 3 * 256 * E),
 // where last blocks are a large share of the tiles. Both calls derive it from the same config.
 inline bool plan_wide_tails(const moe_config* c, int tile_m) {
   if (tile_m != 256 || (c->flags & MOE_FLAG_NO_WIDE_TAILS)) return false;
   if (c->flags & MOE_FLAG_WIDE_TAILS) return true;
-  return (long long)c->T * c->k <= 2ll * 256 * c->E;
+  return (long long)c->T * c->k <= 3ll * 256 * c->E;
 }
 // Burst-Gap microbenchmark: `producers` workgroups, each storing `bytes` per burst into its own
 // `region` of buf, `periods` times, with a busy gap of `gap_ticks` real-time counter ticks.

@@ -252,10 +252,10 @@ def test_all_orders_grids_and_tiles_byte_identical(workload):
 # not, even and odd (and partial) n-tile counts.
 WIDE_SHAPES = [
     # counts about 1024: five experts end in a block of at most 128 rows; n1 = 4, n2 = 1; the
-    # default would not choose wide blocks here (T k > 512 E)
+    # default would not choose wide blocks here (T k > 768 E)
     LONG,
     # counts about 400: two experts end in a block of at most 128 rows; n1 = 3, n2 = 2; chosen
-    # by default (T k <= 512 E)
+    # by default (T k <= 768 E)
     W.shape(T=1200, H=384, I=320, E=6, k=2, experts_per_wave=2, seed=44, x_std=1.0, w_std=0.05),
 ]
 
@@ -292,7 +292,7 @@ def test_wide_tail_tiles_byte_identical(which):
         cfg = make_cfg(shape, tile_m=256, **v)
         bufs = run(cfg, dev, gather=gather)
         flags = v.get("flags", 0)
-        auto = shape.T * shape.k <= 512 * shape.E
+        auto = shape.T * shape.k <= 768 * shape.E
         if flags == ON or (flags == 0 and auto):
             assert wide_records(cfg, bufs) > 0
         else:
