@@ -321,22 +321,44 @@ def test_repeated_calls_reuse_buffers(workload):
         assert np.array_equal(first[key], again[key])
 
 
-def test_bounded_wait_reports_timeout_and_recovers(workload):
+@pytest.mark.parametrize("wide", [False, True])
+def test_bounded_wait_reports_timeout_and_recovers(workload, wide):
     d, dev = workload
     small = W.shape(T=64, H=128, I=128, E=4, k=2, experts_per_wave=2, seed=42)
     ds = W.generate(small)
     dv = Device(ds)
-    cfg = make_cfg(small, flags=moe.MOE_FLAG_FORCE_WAIT_TIMEOUT, spin_limit=20)
+    # wide: 256-row tiles with every (short) m-block wide, on the kernel instance that runs them
+    extra = dict(tile_m=256) if wide else {}
+    flags = moe.MOE_FLAG_WIDE_TAILS if wide else 0
+    cfg = make_cfg(small, flags=flags | moe.MOE_FLAG_FORCE_WAIT_TIMEOUT, spin_limit=20, **extra)
     bufs = moe.alloc_buffers(cfg)
-    note("forced bounded-wait timeout")
+    note(f"forced bounded-wait timeout wide={wide}")
     run(cfg, dv, bufs, check_status=False)
     assert moe.moe_status_read(bufs["ws"]) == moe.MOE_ERR_TIMEOUT
-    cfg_ok = make_cfg(small)
+    cfg_ok = make_cfg(small, flags=flags, **extra)
     run(cfg_ok, dv, bufs)  # asserts MOE_OK
     o = R.moe_layer(ds["x"], ds["logits"], ds["w1"], ds["w2"], small.k)
     g = fetch(bufs, keys=("out",))
     from tests.gpu_util import assert_close_rel
     assert_close_rel(g["out"], o["out"], what="after recovery")
+
+
+def test_repeated_calls_reuse_buffers_wide():
+    # the wide-capable instance resets its counters and cursors for the next call as well
+    shape = WIDE_SHAPES[1]
+    d = W.generate(shape)
+    dev = Device(d)
+    cfg = make_cfg(shape, schedule=1, tile_m=256, flags=moe.MOE_FLAG_WIDE_TAILS)
+    bufs = moe.alloc_buffers(cfg)
+    note("repeated calls, wide last m-blocks")
+    first = fetch(run(cfg, dev, bufs), keys=("yd", "out"))
+    assert wide_records(cfg, bufs) > 0
+    for _ in range(2):
+        moe.moe_forward(cfg, bufs["xd"], dev.w1, dev.w2, bufs["act"], bufs["yd"], bufs["ws"])
+        assert moe.moe_status_read(bufs["ws"]) == moe.MOE_OK
+    again = fetch(run(cfg, dev, bufs), keys=("yd", "out"))
+    for key in first:
+        assert np.array_equal(first[key], again[key])
 
 
 def test_dispatch_on_side_stream_orders_with_plan(workload):
