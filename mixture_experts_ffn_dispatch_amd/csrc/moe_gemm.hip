@@ -55,7 +55,11 @@ __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint3
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, soffset, 0, 0);
 }
 
-__device__ inline float silu(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
+// IEEE division: the result is rounded to bf16 right after, and 1 + e^-g is exactly 1 for
+// g >= 17, so silu(g) = g exactly there, as with the division. It takes 6 instead of about 14
+// vector instructions for each of the 64 outputs a lane forms in a Linear-1 epilogue.
+__device__ inline float silu(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 // LDS swizzle of a 128-byte operand row: its eight 16-byte chunks are permuted by XOR with
 // (row & 7) ^ (bit 3 of row). Any 8 consecutive rows then put one chunk index in 8 distinct
