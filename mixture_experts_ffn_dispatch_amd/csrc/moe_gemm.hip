@@ -10,7 +10,8 @@
 //    record), so each group's tiles start in list order whatever the grid size.
 //  * Linear-1 tile (expert e, m-block, n-tile): 128 gate rows + the matching 128 up rows of
 //    W1[e] against up to tile_m dispatched rows; the epilogue forms
-//    A = bf16(silu(gate) * up) for 128 columns and releases the m-block's ready counter.
+//    A = bf16(silu(gate) * up) for 128 columns; the m-block's ready counter is released, two
+//    Linear-1 tiles at a time (or before the workgroup takes a Linear-2 tile or exits).
 //  * Linear-2 tile: waits (bounded) until all Linear-1 tiles of its m-block have released,
 //    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
 //  * Wide last m-blocks (a second instance of the 256-row kernel): an m-block of at most 128
@@ -132,6 +133,25 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   // (the list bounds load alongside it) and one 16-byte record load.
   const int my_group = (int)(blockIdx.x % (unsigned)p.ngroups);
   int scan_group = 0;  // thread 0 only: groups whose lists are used up
+  // Linear-1 completions are released in batches of kReleaseBatch: one drain of the stores and
+  // one agent-scope release (an L2 write-back) for several m-block counters. A workgroup holds
+  // completions only while it runs Linear-1 tiles, which never wait; it releases them before
+  // any Linear-2 tile (which may wait) and before it exits, so no wait depends on a held one.
+  int npend = 0;                     // completions held (the same value in every lane)
+  int pend_mb[kReleaseBatch] = {};  // thread 0: their m-blocks
+  auto release = [&]() {
+    // every wavefront drains its own stores first (a workgroup barrier alone does not wait
+    // for them), then one lane releases at agent scope and bumps the counters
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#pragma unroll
+      for (int i = 0; i < kReleaseBatch; ++i)
+        if (i < npend) __hip_atomic_fetch_add(&p.mb_ready[pend_mb[i]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    npend = 0;
+  };
   for (;;) {
     if (tid == 0) {
       i32x4 rec = {kNoTask, -1, 0, 0};  // task word, expert, first row, rows
@@ -173,6 +193,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     __syncthreads();
     // the task and its m-block record are the same for the whole workgroup: keep them scalar
     const int task = __builtin_amdgcn_readfirstlane(s_task[0]);
+    if (npend > 0 && (task == kNoTask || ((unsigned)task >> kTaskL2Bit) != 0u)) release();
     if (task == kNoTask) break;
     const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
     const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
@@ -421,12 +442,13 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       }
     }
 
-    if (!l2) {
-      // publish this tile's A columns: every wavefront drains its own stores first (a
-      // workgroup barrier alone does not wait for them), then one lane releases at agent scope
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(&p.mb_ready[mb], 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    if (!l2) {  // hold this tile's completion; release when the batch is full
+      if (tid == 0) {
+#pragma unroll
+        for (int i = 0; i < kReleaseBatch; ++i)
+          if (i == npend) pend_mb[i] = mb;
+      }
+      if (++npend == kReleaseBatch) release();
     }
     __syncthreads();
   }

@@ -51,6 +51,7 @@ constexpr int kTaskMblkShift = 12;
 constexpr int kTaskMblkBits = 19;
 constexpr int kTaskNtMask = 0xFFF;
 constexpr int kDefaultSpinLimit = 1 << 22;
+constexpr int kReleaseBatch = 2;  // Linear-1 completions a GEMM workgroup releases together
 // "no more tiles": all ones. Never a real task because m-block 0x7FFFF is out of range
 // (the host rejects plans with 2^19 - 1 or more m-blocks).
 constexpr int32_t kNoTask = -1;
