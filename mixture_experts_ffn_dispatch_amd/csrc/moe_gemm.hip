@@ -137,6 +137,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   // one agent-scope release (an L2 write-back) for several m-block counters. A workgroup holds
   // completions only while it runs Linear-1 tiles, which never wait; it releases them before
   // any Linear-2 tile (which may wait) and before it exits, so no wait depends on a held one.
+  // Holding delays a release by up to one Linear-1 tile, which costs nothing only when the
+  // Linear-2 tiles that wait for it lie a whole wave later in the list: an interleaved order
+  // with a lead of at least two waves. Otherwise every completion is released at once.
+  const int batch = p.hdr[HDR_LEAD] >= 2 ? kReleaseBatch : 1;
   int npend = 0;                     // completions held (the same value in every lane)
   int pend_mb[kReleaseBatch] = {};  // thread 0: their m-blocks
   auto release = [&]() {
@@ -448,7 +452,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         for (int i = 0; i < kReleaseBatch; ++i)
           if (i == npend) pend_mb[i] = mb;
       }
-      if (++npend == kReleaseBatch) release();
+      if (++npend >= batch) release();
     }
     __syncthreads();
   }
