@@ -2,7 +2,7 @@
 
     python -m mixture_experts_ffn_dispatch_amd.prof_summary trace  <kernel_stats.csv> <out.txt> <command...>
     python -m mixture_experts_ffn_dispatch_amd.prof_summary counters <counter_collection.csv> <out.txt> <command...>
-    python -m mixture_experts_ffn_dispatch_amd.prof_summary traffic <fetch.csv> <write.csv> <workload> <out.json> <kernel_sha>
+    python -m mixture_experts_ffn_dispatch_amd.prof_summary traffic <fetch.csv> <write.csv> <workload> <out.json> <kernel_sha> <command...>
 
 Counter values are averaged per kernel over the dispatches in the file. For the traffic
 summary, FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the persistent GEMM are scaled by
@@ -62,6 +62,7 @@ def main():
                 f.write(f"{k:28s} {n:28s} {v:16.6g}\n")
     elif mode == "traffic":
         fetch, write, workload, out, sha = sys.argv[2:7]
+        cmd = " ".join(sys.argv[7:])  # the profiled command; run once with each counter
         cf, cw = counters(fetch), counters(write)
         copy_bytes = 1024 * 1024 * 1024
         f_scale = copy_bytes / (cf[("copyBuffer", "FETCH_SIZE")] * 1024)
@@ -69,6 +70,7 @@ def main():
         fb = cf[("gemm_persistent_kernel", "FETCH_SIZE")] * 1024 * f_scale
         wb = cw[("gemm_persistent_kernel", "WRITE_SIZE")] * 1024 * w_scale
         rec = {"kernel": "gemm_persistent_kernel", "workload": workload, "kernel_sha": sha,
+               "commands": [cmd.replace("<COUNTER>", c) for c in ("FETCH_SIZE", "WRITE_SIZE")],
                "fetch_size_kib": cf[("gemm_persistent_kernel", "FETCH_SIZE")],
                "write_size_kib": cw[("gemm_persistent_kernel", "WRITE_SIZE")],
                "fetch_scale": f_scale, "write_scale": w_scale,
