@@ -449,9 +449,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
 
   // 4. write the tile list and the unit table. Inside a run the tiles of each expert are cut
   //    into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted block by block
-  //    (m-block major inside a block), so neighbouring positions share operand rows. Every
-  //    tile of a phase is placed independently: tile u of the phase is (m-block u / n, n-tile
-  //    u % n); its expert comes from the m-block table in LDS (or a binary search over s_mb
+  //    (n-tile major inside a block: consecutive positions share a weight slab, which the
+  //    workgroups of an XCD then read while it is still in their L2). Every tile of a phase is
+  //    placed independently: tile u of the phase is (m-block u / n, n-tile u % n); its expert comes from the m-block table in LDS (or a binary search over s_mb
   //    when there are more m-blocks than the table holds). In a merged segment, Linear-1
   //    unit v goes right after Linear-2 unit ceil((v+1) * bu / au) (bu, au: unit counts), which
   //    spreads the Linear-1 units evenly and ends the segment with the last Linear-1 unit.
@@ -481,7 +481,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
       const int mg = ml / kBlockM, ng = nt / kBlockN;
       const int bm_act = min(kBlockM, nmb - mg * kBlockM), bn_act = min(kBlockN, n - ng * kBlockN);
       const int q = (s_mb[e] - s_mb[w * W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
-                    (ml - mg * kBlockM) * bn_act + (nt - ng * kBlockN);
+                    (nt - ng * kBlockN) * bm_act + (ml - mg * kBlockM);
       const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
       // positions and unit counts stay below 2^31 (the host caps the tile count), so 32-bit
       // unsigned arithmetic is exact here

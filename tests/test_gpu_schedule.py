@@ -30,14 +30,14 @@ BLOCK_M, BLOCK_N, UNIT = 4, 8, 32  # tile blocks of one expert; units of consecu
 
 def run_tiles(phase, wave_experts, mb_of, n):
     """One run's tiles in emission order: per expert, blocks of up to BLOCK_M m-blocks x
-    BLOCK_N n-tiles, m-block major inside a block."""
+    BLOCK_N n-tiles, n-tile major inside a block."""
     out = []
     for e in wave_experts:
         mbs = mb_of[e]
         for m0 in range(0, len(mbs), BLOCK_M):
             for n0 in range(0, n, BLOCK_N):
-                for mb in mbs[m0:m0 + BLOCK_M]:
-                    for nt in range(n0, min(n, n0 + BLOCK_N)):
+                for nt in range(n0, min(n, n0 + BLOCK_N)):
+                    for mb in mbs[m0:m0 + BLOCK_M]:
                         out.append((phase, mb, nt))
     return out
 
