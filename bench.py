@@ -58,7 +58,7 @@ def gemm_bytes(s, counts) -> int:
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("moe_gemm.hip", "moe_internal.h"):
+    for f in ("moe_gemm.hip", "moe_internal.h", "moe_plan.hip"):  # the kernel and the tile order it walks
         with open(os.path.join(ROOT, "mixture_experts_ffn_dispatch_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
