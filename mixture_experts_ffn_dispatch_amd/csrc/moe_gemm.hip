@@ -10,15 +10,17 @@
 //    record), so each group's tiles start in list order whatever the grid size.
 //  * Linear-1 tile (expert e, m-block, n-tile): 128 gate rows + the matching 128 up rows of
 //    W1[e] against up to tile_m dispatched rows; the epilogue forms
-//    A = bf16(silu(gate) * up) for 128 columns; the m-block's ready counter is released, two
-//    Linear-1 tiles at a time (or before the workgroup takes a Linear-2 tile or exits).
+//    A = bf16(silu(gate) * up) for 128 columns; the m-block's ready counter is released (two
+//    Linear-1 tiles at a time when the interleave lead is two waves or more, and always before
+//    the workgroup takes a Linear-2 tile or exits).
 //  * Linear-2 tile: waits (bounded) until all Linear-1 tiles of its m-block have released,
 //    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
 //  * Wide last m-blocks (a second instance of the 256-row kernel): an m-block of at most 128
 //    rows runs as tiles of twice the weight rows by 128 token rows, so an expert's short last
 //    block needs half the tiles and puts no padding rows through the MFMAs.
 //  * The MFMA A operand is the weight tile and the B operand the token tile, so one lane
-//    ends with four consecutive output columns of one token row (8-byte stores).
+//    ends with four consecutive output columns of one token row; the epilogue stages them in
+//    LDS and stores whole row segments (16 bytes per lane).
 //  * Operands go from global memory straight into LDS (buffer->LDS loads) in 64-wide K steps,
 //    double buffered, the 16-byte chunks of each row XOR-swizzled so that 128-bit fragment
 //    reads are free of bank conflicts.
