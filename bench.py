@@ -57,10 +57,15 @@ def gemm_bytes(s, counts) -> int:
 
 
 def kernel_source_sha() -> str:
+    """Hash of the code (comments and blank lines left out) of the GEMM and of the planner that
+    writes the tile order it walks: the profiled traffic belongs to exactly this code."""
     h = hashlib.sha256()
-    for f in ("moe_gemm.hip", "moe_internal.h", "moe_plan.hip"):  # the kernel and the tile order it walks
-        with open(os.path.join(ROOT, "mixture_experts_ffn_dispatch_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in ("moe_gemm.hip", "moe_internal.h", "moe_plan.hip"):
+        with open(os.path.join(ROOT, "mixture_experts_ffn_dispatch_amd", "csrc", f), encoding="utf-8") as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
