@@ -661,18 +661,21 @@ __device__ inline unsigned pack_bf16(float lo, float hi) {
          ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
-// Combine: a wavefront per token. Slot j's row and weight are held by lane j (k <= 64) and
-// broadcast with readlane; each lane takes two 16-byte chunks of the row per step and issues
-// the loads of up to KB slots before any is accumulated, so their latencies overlap. Every Yd
-// row is read exactly once, so the loads are non-temporal. The sum runs over j in ascending
-// order for every element.
+// Combine: a wavefront per (token, column segment); a token's row is cut into `segs` segments
+// when there are too few tokens to fill the GPU. Slot j's row and weight are held by lane j
+// (k <= 64) and broadcast with readlane; each lane takes two 16-byte chunks of the row per
+// step and issues the loads of up to KB slots before any is accumulated, so their latencies
+// overlap. Every Yd row is read exactly once, so the loads are non-temporal. The sum runs over
+// j in ascending order for every element.
 template <int KB>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const float* w,
                                                       const uint16_t* yd, uint16_t* out, int T,
-                                                      int H, int k, int R) {
+                                                      int H, int k, int R, int segs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int cpr = H / 8;
-  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
+  const int cpr = H / 8;                   // 16-byte chunks per row
+  const int cps = (cpr + segs - 1) / segs;  // chunks per segment
+  for (int item = blockIdx.x * 4 + wave; item < T * segs; item += gridDim.x * 4) {
+    const int t = item / segs, c_lo = (item % segs) * cps, c_hi = min(cpr, c_lo + cps);
     int rv = 0;
     float wv = 0.f;
     if (lane < k) {
@@ -683,8 +686,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* pos, const 
         wv = 0.f;
       }
     }
-    for (int c = lane; c < cpr; c += 128) {
-      const bool two = c + 64 < cpr;
+    for (int c = c_lo + lane; c < c_hi; c += 128) {
+      const bool two = c + 64 < c_hi;
       float a0[8], a1[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) a0[i] = a1[i] = 0.f;
@@ -785,8 +788,14 @@ hipError_t launch_dispatch(const int32_t* pos, const uint16_t* x, uint16_t* xd, 
 
 hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd, uint16_t* out, int T,
                           int H, int k, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel<8>, dim3(grid_rows((T + 3) / 4)), dim3(256), 0, s, pos, w, yd, out, T,
-                     H, k, T * k);
+  // with few tokens, cut rows into up to 4 segments of at least 128 chunks (one step of a
+  // wavefront) so that about 4096 wavefronts run
+  const int cpr = H / 8;
+  int segs = (4096 + T - 1) / T;
+  segs = segs < 1 ? 1 : segs > 4 ? 4 : segs;
+  while (segs > 1 && cpr / segs < 128) --segs;
+  hipLaunchKernelGGL(combine_kernel<8>, dim3(grid_rows(((long long)T * segs + 3) / 4)), dim3(256), 0, s, pos, w, yd,
+                     out, T, H, k, T * k, segs);
   return hipGetLastError();
 }
 
