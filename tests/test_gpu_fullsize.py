@@ -78,3 +78,18 @@ def test_full_size_sampled_parity(name):
             assert_close_rel(yd[rows[i, j]], y_ref[i, j], what=f"Yd token {toks[i]} slot {j}")
     assert_close_rel(out[toks], out_ref, what="out (sampled)")
     note("  ok")
+
+
+@pytest.mark.parametrize("name", ["dsv3_share", "qwen3_30b_a3b"])
+def test_full_size_wide_blocks_byte_identical(name):
+    # wide last m-blocks (forced on, and off) at full size, in the benchmark's launch
+    # configuration: the long K loops and the many tiles give the same bytes either way
+    s = W.shape(name)
+    note(f"wide last m-blocks, full size {W.describe(s)}")
+    dev = Device(W.generate(s))
+    outs = []
+    for flags in (moe.MOE_FLAG_WIDE_TAILS, moe.MOE_FLAG_NO_WIDE_TAILS):
+        b = run(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED, flags=flags), dev, gather=True)
+        outs.append({k: b[k] for k in ("act", "yd", "out")})
+    for key in ("act", "yd", "out"):
+        assert torch.equal(outs[0][key].view(torch.int16), outs[1][key].view(torch.int16)), key
