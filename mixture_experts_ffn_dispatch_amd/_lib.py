@@ -12,6 +12,7 @@ from dataclasses import dataclass, field
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
+ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -46,7 +47,7 @@ class CRouting(ctypes.Structure):
 class CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
-        "tasks", "unit_start", "group_units", "group_tasks")] + [(n, ctypes.c_int32) for n in (
+        "tasks", "unit_start", "group_units", "group_tasks", "wave_table")] + [(n, ctypes.c_int32) for n in (
             "chunks", "chunk_tokens", "max_mblk", "max_tasks", "max_slots", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
             "n2_tiles")]
 
@@ -118,6 +119,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.moe_abi_version() != ABI_VERSION:  # the structures below would be misread
+        raise ImportError(f"{path} has ABI version {lib.moe_abi_version()}, this binding needs {ABI_VERSION}: "
+                          "rebuild it")
     _lib = lib
     return lib
 

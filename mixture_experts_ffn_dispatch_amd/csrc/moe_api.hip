@@ -98,6 +98,8 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->max_slots = (int32_t)max_slots;
   L->group_tasks = off;
   off = align_up(off + (size_t)max_slots * 16, 256);
+  L->wave_table = off;
+  off = align_up(off + ((size_t)kWaveTableHead + 9 * ((size_t)c->E + 1)) * 4, 256);
   L->total_bytes = off;
   return MOE_OK;
 }
@@ -195,6 +197,7 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   a.unit_start = at<int32_t>(ws, L.unit_start);
   a.group_units = at<int32_t>(ws, L.group_units);
   a.gtasks = at<int32_t>(ws, L.group_tasks);
+  a.wtab = at<int32_t>(ws, L.wave_table);
   a.max_units = L.max_tasks;
   a.T = cfg->T;
   a.E = cfg->E;

@@ -42,6 +42,9 @@ constexpr int kGroups = 8;
 constexpr int kUnit = 32;
 constexpr int kBlockM = 4;
 constexpr int kBlockN = 8;
+// The planner's wave table (per-wave tile counts, unit prefix sums and run starts, and each
+// expert's first m-block): a head of kWaveTableHead ints, then at most 9 (E + 1) entries.
+constexpr int kWaveTableHead = 24;
 
 constexpr int kTileN2 = 256;         // Linear-2 tile: Yd columns
 constexpr int kTileN1 = 128;         // Linear-1 tile: A columns (=> 128 gate + 128 up weight rows)
@@ -87,6 +90,7 @@ struct PlanArgs {
   int32_t* unit_start;  // [max_units + 1]: list position of each unit's first tile
   int32_t* group_units; // [max_units]: each group's units in list order, groups one after another
   int32_t* gtasks;      // [slots][4]: each group's tile records (kUnit slots per unit), groups one after another
+  int32_t* wtab;        // the wave table: per-wave tile counts and list positions for the tile placement
   int max_units;
   int T, E, k, chunks, chunk_tokens;
   int cstride;   // row stride of chunk_counts: chunks rounded up to a multiple of 4 (16 B)

@@ -12,10 +12,14 @@
 //   scan_schedule  one workgroup: per-expert exclusive scans of the count table (one
 //                  wavefront per expert row), which give every (expert, chunk) its first row
 //                  within the expert and every expert its count; the expert offsets, the
-//                  m-block table, zeroed dependency counters and the tile list.
+//                  m-block table and zeroed dependency counters; then, on one wavefront when
+//                  there are at most 64 expert waves, the per-wave tile counts, the lead and
+//                  where each wave's runs start (the wave table, written to the workspace).
 //   scatter        one block per chunk, its slots split into 16 consecutive runs, one per
 //                  wavefront: per-run expert counts, a per-expert prefix over the runs, then
 //                  stable ranks (ballot/match over 64 slots at a time) give perm and pos.
+//                  Then every block places its share of the tile list and the group records
+//                  from the wave table (each tile independently).
 //
 // The dispatch gather and the combine are in moe_combine.hip.
 #include <math.h>
@@ -178,7 +182,6 @@ __global__ __launch_bounds__(kPlanThreads) void route_small_kernel(PlanArgs a) {
 
 constexpr int kScanThreads = 1024;
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-constexpr int kMbExpertLds = 8192;  // m-blocks whose expert the tile placement looks up in LDS
 
 __device__ inline int units_of(int tiles) { return (tiles + kUnit - 1) / kUnit; }
 
@@ -232,25 +235,198 @@ __device__ int block_min(int v, int* s_tmp) {
   return w;
 }
 
+// The wave table: what the tile placement (step 4, in scatter_kernel) needs from the schedule
+// builder, written to the workspace by scan_schedule_kernel. A head of kWaveTableHead ints
+// (the scalars below and the group offsets), then eight arrays of nw + 1 entries indexed by
+// expert wave, then the first m-block of each expert (E + 1 entries, the last = all m-blocks).
+enum : int { kWtLead = 0, kWtL1Units = 1, kWtL2Units = 2, kWtUnits = 3, kWtGoff = 8 };
+static_assert(kWtGoff + kGroups + 1 <= kWaveTableHead, "wave table head");
+struct WaveTable {
+  int* head;
+  int* a;    // Linear-1 tiles of each wave
+  int* b;    // Linear-2 tiles of each wave
+  int* p1;   // Linear-1 units of all earlier waves
+  int* p2;   // Linear-2 units of all earlier waves
+  int* l1s;  // list position of each wave's Linear-1 run
+  int* l2s;  // list position of each wave's Linear-2 run
+  int* l1u;  // unit index of each wave's first Linear-1 unit
+  int* l2u;  // unit index of each wave's first Linear-2 unit
+  int* mb;   // first m-block of each expert
+  __device__ WaveTable(int* t, int nw) : head(t) {
+    int* p = t + kWaveTableHead;
+    a = p;
+    b = a + nw + 1;
+    p1 = b + nw + 1;
+    p2 = p1 + nw + 1;
+    l1s = p2 + nw + 1;
+    l2s = l1s + nw + 1;
+    l1u = l2s + nw + 1;
+    l2u = l1u + nw + 1;
+    mb = l2u + nw + 1;
+  }
+};
+__device__ inline int wave_table_len(int nw, int E) { return kWaveTableHead + 8 * (nw + 1) + E + 1; }
+
+// Scans and minima for step 3: over wavefront 0 alone (ONE, at most 64 expert waves; no
+// barriers), else over the whole workgroup.
+template <bool ONE>
+__device__ inline int step_scan(int v, int* s_tmp, int& total) {
+  if constexpr (ONE) {
+    const int x = wave_inclusive_scan(v);
+    total = __builtin_amdgcn_readlane(x, 63);
+    return x - v;
+  } else {
+    return block_exclusive_scan(v, s_tmp, total);
+  }
+}
+template <bool ONE>
+__device__ inline int step_min(int v, int* s_tmp) {
+  if constexpr (ONE) return wave_min(v);
+  else return block_min(v, s_tmp);
+}
+template <bool ONE>
+__device__ inline void step_sync() {
+  if constexpr (!ONE) __syncthreads();
+}
+
+// 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
+//    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
+//    last unit may be shorter); the orders are defined on units, so every unit is one
+//    contiguous stretch of the list holding tiles of a single run. Thread i handles wave i.
+template <bool ONE>
+__device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, int* s_tmp) {
+  const int tid = threadIdx.x, E = a.E, W = a.W;
+  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  int aw = 0, bw = 0;
+  if (tid < nw) {
+    const int m = t.mb[min(E, (tid + 1) * W)] - t.mb[tid * W];
+    aw = m * a.n1;
+    bw = m * a.n2;
+    t.a[tid] = aw;
+    t.b[tid] = bw;
+  }
+  step_sync<ONE>();
+  // Lead 0 picks D from the tile counts. A Linear-2 tile of wave i must not be taken before
+  // the last Linear-1 tile of wave i has finished. With `grid` tiles in flight, list
+  // positions are taken at about grid per mean tile duration, so a Linear-1 tile finishes
+  // about grid * t1 / t_mean positions after it was taken (t1, t_mean: Linear-1 and mean
+  // tile durations, proportional to K = H for Linear-1 and I for Linear-2). In the interleaved
+  // list the last Linear-1 tile of wave i ends segment i - D (or the lead prefix) and Linear-2
+  // of wave i starts segment i, so with a_j, b_j the Linear-1 / Linear-2 tiles of wave j and
+  // PA, PB their prefix sums the tiles between them number
+  //   dist_i(D) = PB[i] - PB[max(0, i - D + 1)] + PA[min(i + D, nw)] - PA[min(i + 1, nw)].
+  // D is the smallest lead with dist_i(D) * (A H + B I) >= grid * H * (A + B) for every wave
+  // with Linear-2 tiles (A, B: all Linear-1 / Linear-2 tiles), else nw. The prefix sums use
+  // p1 / p2, which hold unit prefix sums only after the lead is known.
+  int D = a.lead;
+  {
+    int A, B;
+    const int pa = step_scan<ONE>(aw, s_tmp, A);
+    const int pb = step_scan<ONE>(bw, s_tmp, B);
+    if (interleaved && D == 0) {
+      if (tid < nw) {
+        t.p1[tid] = pa;
+        t.p2[tid] = pb;
+      }
+      if (tid == 0) {
+        t.p1[nw] = A;
+        t.p2[nw] = B;
+      }
+      step_sync<ONE>();
+      const long long den = (long long)A * a.H + (long long)B * a.I;
+      const long long need = (long long)a.grid * a.H * (A + B);
+      int cand = nw;  // thread t tests lead t + 1
+      if (tid < nw) {
+        const int Dc = tid + 1;
+        bool ok = true;
+        for (int i = 0; i < nw && ok; ++i) {
+          if (t.b[i] == 0) continue;
+          const long long dist = (long long)t.p2[i] - t.p2[max(0, i - Dc + 1)] + t.p1[min(i + Dc, nw)] -
+                                 t.p1[min(i + 1, nw)];
+          ok = dist * den >= need;
+        }
+        if (ok) cand = Dc;
+      }
+      D = step_min<ONE>(cand, s_tmp);
+    }
+    D = min(max(D, 1), max(nw, 1));
+  }
+  const int auw = units_of(aw), buw = units_of(bw);
+  int n_l1_units, n_l2_units;
+  {
+    const int p1 = step_scan<ONE>(tid < nw ? auw : 0, s_tmp, n_l1_units);
+    const int p2 = step_scan<ONE>(tid < nw ? buw : 0, s_tmp, n_l2_units);
+    if (tid < nw) {
+      t.p1[tid] = p1;
+      t.p2[tid] = p2;
+    }
+    if (tid == 0) {
+      t.p1[nw] = n_l1_units;
+      t.p2[nw] = n_l2_units;
+    }
+  }
+  int total_units;
+  if (!interleaved) {
+    // Expert-Wave order: L1(0) L2(0) L1(1) L2(1) ...
+    int unused;
+    const int st = step_scan<ONE>(aw + bw, s_tmp, unused);
+    const int su = step_scan<ONE>(auw + buw, s_tmp, total_units);
+    if (tid < nw) {
+      t.l1s[tid] = st;
+      t.l2s[tid] = st + aw;
+      t.l1u[tid] = su;
+      t.l2u[tid] = su + auw;
+    }
+  } else {
+    // interleaved: L1(0) .. L1(D-1), then segment i = L2(i) merged with L1(i + D)
+    int prefix_total, prefix_units, unused, seg_units;
+    const bool lead = tid < min(D, nw);
+    const int p = step_scan<ONE>(lead ? aw : 0, s_tmp, prefix_total);
+    const int pu = step_scan<ONE>(lead ? auw : 0, s_tmp, prefix_units);
+    const int a_next = tid + D < nw ? t.a[tid + D] : 0;
+    const int seg = tid < nw ? bw + a_next : 0;
+    const int segu = tid < nw ? buw + units_of(a_next) : 0;
+    const int q = prefix_total + step_scan<ONE>(seg, s_tmp, unused);
+    const int qu = prefix_units + step_scan<ONE>(segu, s_tmp, seg_units);
+    total_units = prefix_units + seg_units;
+    if (tid < nw) {
+      t.l2s[tid] = q;  // segment tid starts with L2(tid)
+      t.l2u[tid] = qu;
+      if (tid < D) {  // lead prefix
+        t.l1s[tid] = p;
+        t.l1u[tid] = pu;
+      }
+      if (tid + D < nw) {  // L1(tid + D) lives in segment tid
+        t.l1s[tid + D] = q;
+        t.l1u[tid + D] = qu;
+      }
+    }
+  }
+  // first entry of each locality group's unit list (group g gets units g, g + G, ... of each
+  // phase)
+  if (tid <= kGroups) {
+    int goff = 0;
+    for (int h = 0; h < tid; ++h)
+      goff += (n_l1_units - h + kGroups - 1) / kGroups + (n_l2_units - h + kGroups - 1) / kGroups;
+    t.head[kWtGoff + tid] = goff;
+  }
+  if (tid == 0) {
+    t.head[kWtLead] = D;
+    t.head[kWtL1Units] = n_l1_units;
+    t.head[kWtL2Units] = n_l2_units;
+    t.head[kWtUnits] = total_units;
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a) {
   __shared__ int s_tmp[32];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];  // expert offsets
   __shared__ int s_cnt[MOE_MAX_EXPERTS];      // rows routed to each expert
-  __shared__ short s_mbe[kMbExpertLds];       // expert of each m-block (when they all fit)
-  __shared__ short s_wave[MOE_MAX_EXPERTS];    // wave of each expert
-  __shared__ int s_goff[kGroups + 1];          // first entry of each group's unit list
-  __shared__ int s_mb[MOE_MAX_EXPERTS + 1];   // first m-block of each expert
-  __shared__ int s_l1s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-1 run
-  __shared__ int s_l2s[MOE_MAX_EXPERTS];      // list position of each wave's Linear-2 run
-  __shared__ int s_l1u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-1 unit
-  __shared__ int s_l2u[MOE_MAX_EXPERTS];      // unit index of each wave's first Linear-2 unit
-  __shared__ int s_p1[MOE_MAX_EXPERTS + 1];   // Linear-1 units of all earlier waves
-  __shared__ int s_p2[MOE_MAX_EXPERTS + 1];   // Linear-2 units of all earlier waves
-  __shared__ int s_a[MOE_MAX_EXPERTS];        // Linear-1 tiles per wave
-  __shared__ int s_b[MOE_MAX_EXPERTS];        // Linear-2 tiles per wave
+  __shared__ int s_tab[kWaveTableHead + 9 * (MOE_MAX_EXPERTS + 1)];  // the wave table
   const int tid = threadIdx.x;
   const int E = a.E, BM = a.tile_m;
-
+  const int nw = (E + a.W - 1) / a.W;
+  const WaveTable t(s_tab, nw);
   // 1. per-expert exclusive scans of the (expert, chunk) count table, in place: entry (e, c)
   //    becomes the first row of chunk c's slots among expert e's rows (the scatter adds the
   //    expert's offset), and the row total is the expert's count. Wavefront w owns rows
@@ -313,242 +489,37 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   for (int e = tid; e <= E; e += kScanThreads) a.offsets[e] = s_off[e];
   int total_mb;
   const int mb0 = block_exclusive_scan(nmb, s_tmp, total_mb);
-  if (tid < E) s_mb[tid] = mb0;
-  if (tid == 0) s_mb[E] = total_mb;
+  if (tid < E) t.mb[tid] = mb0;
+  if (tid == 0) t.mb[E] = total_mb;
   if (tid < E) {
     for (int i = 0; i < nmb; ++i) {
       a.mb_expert[mb0 + i] = tid;
       a.mb_row0[mb0 + i] = s_off[tid] + i * BM;
       const int rows = min(BM, cnt - i * BM);
       a.mb_rows[mb0 + i] = rows | (a.wide_tails && 2 * rows <= BM ? kRowsWide : 0);
-      if (mb0 + i < kMbExpertLds) s_mbe[mb0 + i] = (short)tid;
     }
   }
   for (int i = tid; i < total_mb; i += kScanThreads) a.mb_ready[i] = 0;
   __syncthreads();
 
-  // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
-  //    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
-  //    last unit may be shorter); the orders are defined on units, so every unit is one
-  //    contiguous stretch of the list holding tiles of a single run.
-  const int W = a.W, nw = (E + W - 1) / W;
-  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
-  int aw = 0, bw = 0;
-  if (tid < nw) {
-    const int m = s_mb[min(E, (tid + 1) * W)] - s_mb[tid * W];
-    aw = m * a.n1;
-    bw = m * a.n2;
-    s_a[tid] = aw;
-    s_b[tid] = bw;
-  }
-  __syncthreads();
-  // Lead 0 picks D from the tile counts. A Linear-2 tile of wave i must not be taken before
-  // the last Linear-1 tile of wave i has finished. With `grid` tiles in flight, list
-  // positions are taken at about grid per mean tile duration, so a Linear-1 tile finishes
-  // about grid * t1 / t_mean positions after it was taken (t1, t_mean: Linear-1 and mean
-  // tile durations, proportional to K = H for Linear-1 and I for Linear-2). In the interleaved
-  // list the last Linear-1 tile of wave i ends segment i - D (or the lead prefix) and Linear-2
-  // of wave i starts segment i, so with a_j, b_j the Linear-1 / Linear-2 tiles of wave j and
-  // PA, PB their prefix sums the tiles between them number
-  //   dist_i(D) = PB[i] - PB[max(0, i - D + 1)] + PA[min(i + D, nw)] - PA[min(i + 1, nw)].
-  // D is the smallest lead with dist_i(D) * (A H + B I) >= grid * H * (A + B) for every wave
-  // with Linear-2 tiles (A, B: all Linear-1 / Linear-2 tiles), else nw. The prefix sums use
-  // s_p1 / s_p2, which are filled only after the lead is known.
-  int D = a.lead;
-  {
-    int A, B;
-    const int pa = block_exclusive_scan(aw, s_tmp, A);
-    const int pb = block_exclusive_scan(bw, s_tmp, B);
-    if (interleaved && D == 0) {
-      if (tid < nw) {
-        s_p1[tid] = pa;
-        s_p2[tid] = pb;
-      }
-      if (tid == 0) {
-        s_p1[nw] = A;
-        s_p2[nw] = B;
-      }
-      __syncthreads();
-      const long long den = (long long)A * a.H + (long long)B * a.I;
-      const long long need = (long long)a.grid * a.H * (A + B);
-      int cand = nw;  // thread t tests lead t + 1
-      if (tid < nw) {
-        const int Dc = tid + 1;
-        bool ok = true;
-        for (int i = 0; i < nw && ok; ++i) {
-          if (s_b[i] == 0) continue;
-          const long long dist = (long long)s_p2[i] - s_p2[max(0, i - Dc + 1)] + s_p1[min(i + Dc, nw)] -
-                                 s_p1[min(i + 1, nw)];
-          ok = dist * den >= need;
-        }
-        if (ok) cand = Dc;
-      }
-      D = block_min(cand, s_tmp);
-    }
-    D = min(max(D, 1), max(nw, 1));
-  }
-  const int auw = units_of(aw), buw = units_of(bw);
-  int n_l1_units, n_l2_units;
-  {
-    const int p1 = block_exclusive_scan(tid < nw ? auw : 0, s_tmp, n_l1_units);
-    const int p2 = block_exclusive_scan(tid < nw ? buw : 0, s_tmp, n_l2_units);
-    if (tid < nw) {
-      s_p1[tid] = p1;
-      s_p2[tid] = p2;
-    }
-    if (tid == 0) {
-      s_p1[nw] = n_l1_units;
-      s_p2[nw] = n_l2_units;
-    }
-  }
-  int total_units;
-  if (!interleaved) {
-    // Expert-Wave order: L1(0) L2(0) L1(1) L2(1) ...
-    int unused;
-    const int st = block_exclusive_scan(aw + bw, s_tmp, unused);
-    const int su = block_exclusive_scan(auw + buw, s_tmp, total_units);
-    if (tid < nw) {
-      s_l1s[tid] = st;
-      s_l2s[tid] = st + aw;
-      s_l1u[tid] = su;
-      s_l2u[tid] = su + auw;
-    }
+  // 3. on wavefront 0 alone when it can (the common case: a few expert waves)
+  if (nw <= 64) {
+    if (tid < 64) schedule_waves<true>(a, t, nw, s_tmp);
   } else {
-    // interleaved: L1(0) .. L1(D-1), then segment i = L2(i) merged with L1(i + D)
-    int prefix_total, prefix_units, unused, seg_units;
-    const bool lead = tid < min(D, nw);
-    const int p = block_exclusive_scan(lead ? aw : 0, s_tmp, prefix_total);
-    const int pu = block_exclusive_scan(lead ? auw : 0, s_tmp, prefix_units);
-    const int a_next = tid + D < nw ? s_a[tid + D] : 0;
-    const int seg = tid < nw ? bw + a_next : 0;
-    const int segu = tid < nw ? buw + units_of(a_next) : 0;
-    const int q = prefix_total + block_exclusive_scan(seg, s_tmp, unused);
-    const int qu = prefix_units + block_exclusive_scan(segu, s_tmp, seg_units);
-    total_units = prefix_units + seg_units;
-    if (tid < nw) {
-      s_l2s[tid] = q;  // segment tid starts with L2(tid)
-      s_l2u[tid] = qu;
-      if (tid < D) {  // lead prefix
-        s_l1s[tid] = p;
-        s_l1u[tid] = pu;
-      }
-      if (tid + D < nw) {  // L1(tid + D) lives in segment tid
-        s_l1s[tid + D] = q;
-        s_l1u[tid + D] = qu;
-      }
-    }
+    schedule_waves<false>(a, t, nw, s_tmp);
   }
-  // first entry of each locality group's unit list (group g gets units g, g + G, ... of each
-  // phase), and the wave of each expert
-  if (tid <= kGroups) {
-    int goff = 0;
-    for (int h = 0; h < tid; ++h)
-      goff += (n_l1_units - h + kGroups - 1) / kGroups + (n_l2_units - h + kGroups - 1) / kGroups;
-    s_goff[tid] = goff;
-  }
-  for (int e = tid; e < E; e += kScanThreads) s_wave[e] = (short)(e / W);
   __syncthreads();
 
-  // 4. write the tile list and the unit table. Inside a run the tiles of each expert are cut
-  //    into blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted block by block
-  //    (n-tile major inside a block: consecutive positions share a weight slab, which the
-  //    workgroups of an XCD then read while it is still in their L2). Every tile of a phase is
-  //    placed independently: tile u of the phase is (m-block u / n, n-tile u % n); its expert comes from the m-block table in LDS (or a binary search over s_mb
-  //    when there are more m-blocks than the table holds). In a merged segment, Linear-1
-  //    unit v goes right after Linear-2 unit ceil((v+1) * bu / au) (bu, au: unit counts), which
-  //    spreads the Linear-1 units evenly and ends the segment with the last Linear-1 unit.
-  //    Each tile also writes its record into its group's record list, where every unit owns
-  //    kUnit consecutive slots (a short unit's spare slots hold no-op records): so a tile's slot
-  //    is (the unit's index in the groups' unit lists) * kUnit + its offset in the unit.
-  for (int ph = 0; ph < 2; ++ph) {
-    const int n = ph ? a.n2 : a.n1;
-    // tile u = (m-block u / n, n-tile u % n), stepped by kScanThreads without dividing again
-    const int dmb = kScanThreads / n, dnt = kScanThreads % n;
-    int mb = tid / n, nt = tid % n;
-    for (int u = tid; u < total_mb * n; u += kScanThreads) {
-      int e;  // expert e with s_mb[e] <= mb < s_mb[e + 1]
-      if (total_mb <= kMbExpertLds) {
-        e = s_mbe[mb];
-      } else {
-        int lo = 0, hi = E - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (s_mb[mid] <= mb) lo = mid;
-          else hi = mid - 1;
-        }
-        e = lo;
-      }
-      const int w = s_wave[e];
-      const int nmb = s_mb[e + 1] - s_mb[e], ml = mb - s_mb[e];
-      const int mg = ml / kBlockM, ng = nt / kBlockN;
-      const int bm_act = min(kBlockM, nmb - mg * kBlockM), bn_act = min(kBlockN, n - ng * kBlockN);
-      const int q = (s_mb[e] - s_mb[w * W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
-                    (nt - ng * kBlockN) * bm_act + (ml - mg * kBlockM);
-      const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
-      // positions and unit counts stay below 2^31 (the host caps the tile count), so 32-bit
-      // unsigned arithmetic is exact here
-      unsigned at;
-      int unit, other_before;  // other_before: units of the other phase earlier in the list
-      if (!interleaved) {
-        at = (unsigned)(ph ? s_l2s[w] : s_l1s[w]) + q;
-        unit = (ph ? s_l2u[w] : s_l1u[w]) + ur;
-        other_before = ph ? s_p1[w + 1] : s_p2[w];
-      } else if (ph == 0 && w < D) {  // lead prefix
-        at = (unsigned)s_l1s[w] + q;
-        unit = s_l1u[w] + ur;
-        other_before = 0;
-      } else if (ph == 1) {  // Linear-2 unit ur of segment w
-        const int bu = units_of(s_b[w]);
-        const int au = w + D < nw ? units_of(s_a[w + D]) : 0;
-        const int l1_before = au ? (int)((unsigned)ur * au / bu) : 0;  // all full units
-        at = (unsigned)s_l2s[w] + (unsigned)(ur + l1_before) * kUnit + o;
-        unit = s_l2u[w] + ur + l1_before;
-        other_before = s_p1[min(w + D, nw)] + l1_before;
-      } else {  // Linear-1 unit ur of wave w, in segment w - D
-        const int b = s_b[w - D], bu = units_of(b), au = units_of(s_a[w]);
-        const int c = bu ? (int)(((unsigned)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
-        at = (unsigned)s_l1s[w] + (unsigned)ur * kUnit + (c == bu ? b : c * kUnit) + o;
-        unit = s_l1u[w] + ur + c;
-        other_before = s_p2[w - D] + c;
-      }
-      a.tasks[at] = make_task(ph, mb, nt);
-      // Units of each phase are dealt round-robin to the groups in list order: this unit is
-      // number pidx of its phase, so it goes to group pidx % G; its place in that group's list
-      // counts the group's earlier units of both phases.
-      const int pidx = (ph ? s_p2[w] : s_p1[w]) + ur;
-      const int g = pidx % kGroups;
-      const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
-      const size_t slot0 = (size_t)(s_goff[g] + rank) * kUnit;
-      // the record: task word, expert, first dispatched row and rows of the m-block
-      const int cnt_e = s_off[e + 1] - s_off[e];
-      i32x4 rec;
-      rec[0] = make_task(ph, mb, nt);
-      rec[1] = e;
-      rec[2] = s_off[e] + ml * BM;
-      rec[3] = min(BM, cnt_e - ml * BM);
-      if (a.wide_tails && 2 * rec[3] <= BM) {  // a wide m-block: even n-tiles cover two
-        rec[3] |= kRowsWide;
-        if (nt & 1) rec = i32x4{kNopTask, -1, 0, 0};
-      }
-      *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + o)) = rec;
-      if (o == 0) {
-        a.unit_start[unit] = (int)at;
-        a.group_units[s_goff[g] + rank] = unit;
-        const int size = min(kUnit, (ph ? s_b[w] : s_a[w]) - ur * kUnit);
-        for (int q = size; q < kUnit; ++q)  // a short unit's spare slots
-          *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + q)) = i32x4{kNopTask, -1, 0, 0};
-      }
-      mb += dmb;
-      nt += dnt;
-      if (nt >= n) {
-        nt -= n;
-        ++mb;
-      }
-    }
-  }
+  // publish the wave table (scatter_kernel places the tiles from it) and the header
+  for (int i = tid; i < wave_table_len(nw, E); i += kScanThreads) a.wtab[i] = s_tab[i];
   const int total_tiles = total_mb * (a.n1 + a.n2);
+  const int total_units = t.head[kWtUnits];
   if (tid == 0) a.unit_start[total_units] = total_tiles;
-  if (tid <= kGroups) a.hdr[HDR_GTASK_OFF + tid] = s_goff[tid] * kUnit;
+  if (tid <= kGroups) {
+    a.hdr[HDR_GTASK_OFF + tid] = t.head[kWtGoff + tid] * kUnit;
+    a.hdr[HDR_GROUP_OFF + tid] = t.head[kWtGoff + tid];
+  }
+  if (tid < kGroups) a.hdr[HDR_GROUP_CURSOR + tid] = 0;
   if (tid == 0) {
     a.hdr[HDR_ERROR] = 0;
     a.hdr[HDR_CURSOR] = 0;
@@ -559,10 +530,86 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_N2] = a.n2;
     a.hdr[HDR_DONE] = 0;
     a.hdr[HDR_NUNITS] = total_units;
-    a.hdr[HDR_LEAD] = interleaved ? D : 0;
+    a.hdr[HDR_LEAD] = a.schedule == MOE_SCHED_INTERLEAVED ? t.head[kWtLead] : 0;
     a.hdr[HDR_PLAN_GRID] = a.grid;
-    for (int g = 0; g <= kGroups; ++g) a.hdr[HDR_GROUP_OFF + g] = s_goff[g];
-    for (int g = 0; g < kGroups; ++g) a.hdr[HDR_GROUP_CURSOR + g] = 0;
+  }
+}
+
+// 4. one tile of the list and its record. Inside a run the tiles of each expert are cut into
+//    blocks of up to kBlockM m-blocks x kBlockN n-tiles and emitted block by block (n-tile
+//    major inside a block: consecutive positions share a weight slab, which the workgroups of
+//    an XCD then read while it is still in their L2). Every tile is placed independently from
+//    the wave table. In a merged segment, Linear-1 unit v goes right after Linear-2 unit
+//    ceil((v+1) * bu / au) (bu, au: unit counts), which spreads the Linear-1 units evenly and
+//    ends the segment with the last Linear-1 unit. Each tile also writes its record into its
+//    group's record list, where every unit owns kUnit consecutive slots (a short unit's spare
+//    slots hold no-op records): so a tile's slot is (the unit's index in the groups' unit
+//    lists) * kUnit + its offset in the unit.
+__device__ void place_tile(const PlanArgs& a, const WaveTable& t, int nw, int ph, int mb, int nt) {
+  const int n = ph ? a.n2 : a.n1;
+  const int BM = a.tile_m, D = t.head[kWtLead];
+  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  const int e = a.mb_expert[mb];
+  const int w = e / a.W;
+  const int nmb = t.mb[e + 1] - t.mb[e], ml = mb - t.mb[e];
+  const int mg = ml / kBlockM, ng = nt / kBlockN;
+  const int bm_act = min(kBlockM, nmb - mg * kBlockM);
+  const int q = (t.mb[e] - t.mb[w * a.W]) * n + mg * kBlockM * n + ng * bm_act * kBlockN +
+                (nt - ng * kBlockN) * bm_act + (ml - mg * kBlockM);
+  const int ur = q / kUnit, o = q % kUnit;  // unit of the run, offset in the unit
+  // positions and unit counts stay below 2^31 (the host caps the tile count), so 32-bit
+  // unsigned arithmetic is exact here
+  unsigned at;
+  int unit, other_before;  // other_before: units of the other phase earlier in the list
+  if (!interleaved) {
+    at = (unsigned)(ph ? t.l2s[w] : t.l1s[w]) + q;
+    unit = (ph ? t.l2u[w] : t.l1u[w]) + ur;
+    other_before = ph ? t.p1[w + 1] : t.p2[w];
+  } else if (ph == 0 && w < D) {  // lead prefix
+    at = (unsigned)t.l1s[w] + q;
+    unit = t.l1u[w] + ur;
+    other_before = 0;
+  } else if (ph == 1) {  // Linear-2 unit ur of segment w
+    const int bu = units_of(t.b[w]);
+    const int au = w + D < nw ? units_of(t.a[w + D]) : 0;
+    const int l1_before = au ? (int)((unsigned)ur * au / bu) : 0;  // all full units
+    at = (unsigned)t.l2s[w] + (unsigned)(ur + l1_before) * kUnit + o;
+    unit = t.l2u[w] + ur + l1_before;
+    other_before = t.p1[min(w + D, nw)] + l1_before;
+  } else {  // Linear-1 unit ur of wave w, in segment w - D
+    const int b = t.b[w - D], bu = units_of(b), au = units_of(t.a[w]);
+    const int c = bu ? (int)(((unsigned)(ur + 1) * bu + au - 1) / au) : 0;  // L2 units before
+    at = (unsigned)t.l1s[w] + (unsigned)ur * kUnit + (c == bu ? b : c * kUnit) + o;
+    unit = t.l1u[w] + ur + c;
+    other_before = t.p2[w - D] + c;
+  }
+  a.tasks[at] = make_task(ph, mb, nt);
+  // Units of each phase are dealt round-robin to the groups in list order: this unit is
+  // number pidx of its phase, so it goes to group pidx % G; its place in that group's list
+  // counts the group's earlier units of both phases.
+  const int pidx = (ph ? t.p2[w] : t.p1[w]) + ur;
+  const int g = pidx % kGroups;
+  const int rank = pidx / kGroups + (other_before - g + kGroups - 1) / kGroups;
+  const int goff = t.head[kWtGoff + g];
+  const size_t slot0 = (size_t)(goff + rank) * kUnit;
+  // the record: task word, expert, first dispatched row and rows of the m-block
+  const int off_e = a.offsets[e], cnt_e = a.offsets[e + 1] - off_e;
+  i32x4 rec;
+  rec[0] = make_task(ph, mb, nt);
+  rec[1] = e;
+  rec[2] = off_e + ml * BM;
+  rec[3] = min(BM, cnt_e - ml * BM);
+  if (a.wide_tails && 2 * rec[3] <= BM) {  // a wide m-block: even n-tiles cover two
+    rec[3] |= kRowsWide;
+    if (nt & 1) rec = i32x4{kNopTask, -1, 0, 0};
+  }
+  *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + o)) = rec;
+  if (o == 0) {
+    a.unit_start[unit] = (int)at;
+    a.group_units[goff + rank] = unit;
+    const int size = min(kUnit, (ph ? t.b[w] : t.a[w]) - ur * kUnit);
+    for (int s = size; s < kUnit; ++s)  // a short unit's spare slots
+      *reinterpret_cast<i32x4*>(a.gtasks + 4 * (slot0 + s)) = i32x4{kNopTask, -1, 0, 0};
   }
 }
 
@@ -626,6 +673,23 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
   }
   __syncthreads();
   rank_run<true>(a, f0, f1, run[wave]);
+
+  // 4. the tile list: tile u of all (m-block, n-tile) pairs, Linear-1 then Linear-2, goes to
+  //    block u % blocks; the wave table is copied into `run`, which is free again
+  const int nw = (a.E + a.W - 1) / a.W, len = wave_table_len(nw, a.E);
+  const int total_mb = a.wtab[len - 1], t1 = total_mb * a.n1, total = t1 + total_mb * a.n2;
+  if ((int)blockIdx.x >= total) return;
+  int* s_tab = &run[0][0];
+  __syncthreads();
+  for (int i = tid; i < len; i += kPlanThreads) s_tab[i] = a.wtab[i];
+  __syncthreads();
+  const WaveTable t(s_tab, nw);
+  for (int u = blockIdx.x + gridDim.x * tid; u < total; u += gridDim.x * kPlanThreads) {
+    const int ph = u >= t1 ? 1 : 0;
+    const int n = ph ? a.n2 : a.n1, v = u - ph * t1;
+    const int mb = v / n;
+    place_tile(a, t, nw, ph, mb, v - mb * n);
+  }
 }
 
 }  // namespace

@@ -25,7 +25,18 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.abi_version() == 2
+    assert moe.abi_version() == 3
+
+
+
+def test_binding_matches_header():
+    """The ctypes structures list the header's fields in order, and both name one ABI version."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    assert int(re.search(r"#define MOE_ABI_VERSION (\d+)", text).group(1)) == _lib.ABI_VERSION
+    for struct, cls in (("moe_config", _lib.CConfig), ("moe_routing", _lib.CRouting),
+                        ("moe_ws_layout", _lib.CLayout), ("moe_burst_cfg", _lib.CBurstCfg)):
+        body = re.search(r"typedef struct " + struct + r" \{(.*?)\} " + struct + ";", text, flags=re.S).group(1)
+        assert re.findall(r"(\w+)(?:\[\d+\])?;", body) == [n for n, _ in cls._fields_], struct
 
 
 def test_strerror():
