@@ -81,6 +81,8 @@ SWEEP = [
     (300, 192, 384, 3, 1, 1, 256),
     (300, 64, 64, 1024, 32, 128, 0),  # the largest E and k the ABI accepts
     (129, 128, 64, 1000, 17, 125, 32),
+    (300, 64, 64, 1024, 32, 1, 0),  # 1024 expert waves: the planner's workgroup-wide wave table
+    (129, 128, 64, 100, 6, 1, 32),  # 100 expert waves
 ]
 
 

@@ -114,6 +114,19 @@ def long_workload():
     return Device(W.generate(LONG))
 
 
+# Many expert waves: the planner builds its per-wave table on one wavefront up to 64 waves and
+# with the whole workgroup above that; EDGE sits at the limit, MANY above it (some waves empty).
+EDGE = W.shape(T=600, H=128, I=128, E=128, k=4, experts_per_wave=2, seed=46, x_std=1.0, w_std=0.05)
+MANY = W.shape(T=600, H=128, I=128, E=136, k=4, experts_per_wave=2, seed=45, x_std=1.0, w_std=0.05)
+
+
+@pytest.fixture(scope="module")
+def wave_workloads():
+    many = W.generate(MANY)
+    many["logits"][:, 100:102] -= 40.0  # experts 100 and 101 get no rows: wave 50 is empty
+    return {"edge": Device(W.generate(EDGE)), "many": Device(many)}
+
+
 def auto_lead(counts, tile_m, n1, n2, W_, H, I, grid):
     """The lead moe_plan picks for lead_waves = 0: the smallest D at which, for every wave i
     with Linear-2 tiles, the tiles between the last Linear-1 tile of wave i and its first
@@ -150,9 +163,11 @@ def auto_lead(counts, tile_m, n1, n2, W_, H, I, grid):
 
 @pytest.mark.parametrize("schedule,lead", [(0, 0), (1, 1), (1, 2), (1, 3), (1, 9), (1, 0)])
 @pytest.mark.parametrize("tile_m", [32, 128, 256])
-@pytest.mark.parametrize("which", ["short", "long"])
-def test_task_list_matches_model(workload, long_workload, which, schedule, lead, tile_m):
-    shape, dev = (SHAPE, workload[1]) if which == "short" else (LONG, long_workload)
+@pytest.mark.parametrize("which", ["short", "long", "edge", "many"])
+def test_task_list_matches_model(workload, long_workload, wave_workloads, which, schedule, lead, tile_m):
+    shape, dev = {"short": (SHAPE, workload[1]), "long": (LONG, long_workload), "edge": (EDGE, None),
+                  "many": (MANY, None)}[which]
+    dev = dev or wave_workloads[which]
     # with 256-row tiles, force wide last m-blocks (the long shape would not choose them)
     flags = moe.MOE_FLAG_WIDE_TAILS if tile_m == 256 else 0
     cfg = make_cfg(shape, schedule=schedule, lead_waves=lead, tile_m=tile_m, flags=flags)
