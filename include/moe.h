@@ -151,9 +151,9 @@ typedef struct moe_ws_layout {
                            slots per unit holding its tiles as (task word, expert, first
                            dispatched row, rows), spare slots 0x7FFFFFFE (no-op);
                            group g: slots [header[32+g], header[33+g])             */
-  size_t wave_table;    /* int32[24 + 9 (E + 1)] at most: per expert wave its tile counts,
+  size_t wave_table;    /* int32[24 + 10 (E + 1)] at most: per expert wave its tile counts,
                            unit prefix sums and list positions, and each expert's first
-                           m-block, from which moe_plan places the tiles            */
+                           m-block and first row, from which moe_plan places the tiles */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;

@@ -99,7 +99,7 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->group_tasks = off;
   off = align_up(off + (size_t)max_slots * 16, 256);
   L->wave_table = off;
-  off = align_up(off + ((size_t)kWaveTableHead + 9 * ((size_t)c->E + 1)) * 4, 256);
+  off = align_up(off + ((size_t)kWaveTableHead + 10 * ((size_t)c->E + 1)) * 4, 256);
   L->total_bytes = off;
   return MOE_OK;
 }

@@ -43,7 +43,8 @@ constexpr int kUnit = 32;
 constexpr int kBlockM = 4;
 constexpr int kBlockN = 8;
 // The planner's wave table (per-wave tile counts, unit prefix sums and run starts, and each
-// expert's first m-block): a head of kWaveTableHead ints, then at most 9 (E + 1) entries.
+// expert's first m-block and first row): a head of kWaveTableHead ints, then at most
+// 10 (E + 1) entries.
 constexpr int kWaveTableHead = 24;
 
 constexpr int kTileN2 = 256;         // Linear-2 tile: Yd columns

@@ -69,6 +69,7 @@ __device__ inline unsigned group_max(unsigned x) {
 
 constexpr int kPlanThreads = 1024;  // 16 wavefronts per block in route_hist and scatter
 constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kPlaceBlocks = 256;   // scatter blocks that place the tile list
 
 // Top-k selection, one round per kept slot: the largest key among the candidates (descending
 // logit) is found with group_max, and of the lanes holding it the lowest expert id wins (ties
@@ -238,7 +239,8 @@ __device__ int block_min(int v, int* s_tmp) {
 // The wave table: what the tile placement (step 4, in scatter_kernel) needs from the schedule
 // builder, written to the workspace by scan_schedule_kernel. A head of kWaveTableHead ints
 // (the scalars below and the group offsets), then eight arrays of nw + 1 entries indexed by
-// expert wave, then the first m-block of each expert (E + 1 entries, the last = all m-blocks).
+// expert wave, then the first m-block of each expert (E + 1 entries, the last = all m-blocks)
+// and the expert offsets (E + 1 entries, the last = T k).
 enum : int { kWtLead = 0, kWtL1Units = 1, kWtL2Units = 2, kWtUnits = 3, kWtGoff = 8 };
 static_assert(kWtGoff + kGroups + 1 <= kWaveTableHead, "wave table head");
 struct WaveTable {
@@ -252,7 +254,8 @@ struct WaveTable {
   int* l1u;  // unit index of each wave's first Linear-1 unit
   int* l2u;  // unit index of each wave's first Linear-2 unit
   int* mb;   // first m-block of each expert
-  __device__ WaveTable(int* t, int nw) : head(t) {
+  int* off;  // first dispatched row of each expert
+  __device__ WaveTable(int* t, int nw, int E) : head(t) {
     int* p = t + kWaveTableHead;
     a = p;
     b = a + nw + 1;
@@ -263,9 +266,10 @@ struct WaveTable {
     l1u = l2s + nw + 1;
     l2u = l1u + nw + 1;
     mb = l2u + nw + 1;
+    off = mb + E + 1;
   }
 };
-__device__ inline int wave_table_len(int nw, int E) { return kWaveTableHead + 8 * (nw + 1) + E + 1; }
+__device__ inline int wave_table_len(int nw, int E) { return kWaveTableHead + 8 * (nw + 1) + 2 * (E + 1); }
 
 // Scans and minima for step 3: over wavefront 0 alone (ONE, at most 64 expert waves; no
 // barriers), else over the whole workgroup.
@@ -420,13 +424,13 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
 
 __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a) {
   __shared__ int s_tmp[32];
-  __shared__ int s_off[MOE_MAX_EXPERTS + 1];  // expert offsets
   __shared__ int s_cnt[MOE_MAX_EXPERTS];      // rows routed to each expert
-  __shared__ int s_tab[kWaveTableHead + 9 * (MOE_MAX_EXPERTS + 1)];  // the wave table
+  __shared__ int s_tab[kWaveTableHead + 10 * (MOE_MAX_EXPERTS + 1)];  // the wave table
   const int tid = threadIdx.x;
   const int E = a.E, BM = a.tile_m;
   const int nw = (E + a.W - 1) / a.W;
-  const WaveTable t(s_tab, nw);
+  const WaveTable t(s_tab, nw, E);
+  int* const s_off = t.off;  // expert offsets
   // 1. per-expert exclusive scans of the (expert, chunk) count table, in place: entry (e, c)
   //    becomes the first row of chunk c's slots among expert e's rows (the scatter adds the
   //    expert's offset), and the row total is the expert's count. Wavefront w owns rows
@@ -549,7 +553,12 @@ __device__ void place_tile(const PlanArgs& a, const WaveTable& t, int nw, int ph
   const int n = ph ? a.n2 : a.n1;
   const int BM = a.tile_m, D = t.head[kWtLead];
   const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
-  const int e = a.mb_expert[mb];
+  int e = 0;  // the expert e with t.mb[e] <= mb < t.mb[e + 1] (the last of equal starts)
+  for (int hi = a.E - 1; e < hi;) {
+    const int mid = (e + hi + 1) >> 1;
+    if (t.mb[mid] <= mb) e = mid;
+    else hi = mid - 1;
+  }
   const int w = e / a.W;
   const int nmb = t.mb[e + 1] - t.mb[e], ml = mb - t.mb[e];
   const int mg = ml / kBlockM, ng = nt / kBlockN;
@@ -593,7 +602,7 @@ __device__ void place_tile(const PlanArgs& a, const WaveTable& t, int nw, int ph
   const int goff = t.head[kWtGoff + g];
   const size_t slot0 = (size_t)(goff + rank) * kUnit;
   // the record: task word, expert, first dispatched row and rows of the m-block
-  const int off_e = a.offsets[e], cnt_e = a.offsets[e + 1] - off_e;
+  const int off_e = t.off[e], cnt_e = t.off[e + 1] - off_e;
   i32x4 rec;
   rec[0] = make_task(ph, mb, nt);
   rec[1] = e;
@@ -675,16 +684,19 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
   rank_run<true>(a, f0, f1, run[wave]);
 
   // 4. the tile list: tile u of all (m-block, n-tile) pairs, Linear-1 then Linear-2, goes to
-  //    block u % blocks; the wave table is copied into `run`, which is free again
+  //    block u % nb of the first nb = min(blocks, 256) blocks (about one per CU, all in the
+  //    first round of resident blocks, so later rounds place nothing); the wave table is
+  //    copied into `run`, which is free again
   const int nw = (a.E + a.W - 1) / a.W, len = wave_table_len(nw, a.E);
-  const int total_mb = a.wtab[len - 1], t1 = total_mb * a.n1, total = t1 + total_mb * a.n2;
-  if ((int)blockIdx.x >= total) return;
+  const int total_mb = a.wtab[len - a.E - 2], t1 = total_mb * a.n1, total = t1 + total_mb * a.n2;
+  const int nb = min((int)gridDim.x, kPlaceBlocks);
+  if ((int)blockIdx.x >= min(nb, total)) return;
   int* s_tab = &run[0][0];
   __syncthreads();
   for (int i = tid; i < len; i += kPlanThreads) s_tab[i] = a.wtab[i];
   __syncthreads();
-  const WaveTable t(s_tab, nw);
-  for (int u = blockIdx.x + gridDim.x * tid; u < total; u += gridDim.x * kPlanThreads) {
+  const WaveTable t(s_tab, nw, a.E);
+  for (int u = blockIdx.x + nb * tid; u < total; u += nb * kPlanThreads) {
     const int ph = u >= t1 ? 1 : 0;
     const int n = ph ? a.n2 : a.n1, v = u - ph * t1;
     const int mb = v / n;
