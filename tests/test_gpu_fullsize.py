@@ -15,6 +15,57 @@ import mixture_experts_ffn_dispatch_amd as moe
 pytestmark = pytest.mark.gpu
 
 SAMPLED_TOKENS = 12
+NOP, WIDE = 0x7FFFFFFE, 1 << 30
+
+
+def run_filled(cfg, dev, gather=False):
+    """The layer on buffers whose A, Yd and output start as NaN, so an element no tile wrote
+    shows up."""
+    b = moe.alloc_buffers(cfg, xd=not gather)
+    for key in ("act", "yd", "out"):
+        b[key].fill_(float("nan"))
+    run(cfg, dev, b, gather=gather)
+    for key in ("act", "yd", "out"):
+        assert not torch.isnan(b[key]).any(), f"{key}: elements never written"
+    return b
+
+
+def check_plan(cfg, b):
+    """The plan at full size: the tile list holds every (phase, m-block, n-tile) once, each
+    Linear-2 tile after the Linear-1 tiles of its m-block; the group record lists hold every
+    tile the kernel runs exactly once (the odd n-tiles of wide m-blocks are no-ops), each with
+    its m-block's expert, first row and rows."""
+    L = moe.moe_workspace_layout(cfg)
+    ws = b["ws"].cpu().numpy()
+    hdr = ws[:256].view(np.int32)
+    n, nmb, n1, n2 = (int(hdr[i]) for i in (2, 3, 5, 6))
+    assert n == nmb * (n1 + n2) and n1 == L["n1_tiles"] and n2 == L["n2_tiles"]
+
+    def decode(words):
+        w = words.astype(np.int64) & 0xFFFFFFFF
+        return w >> 31, (w >> 12) & 0x7FFFF, w & 0xFFF
+
+    ph, mb, nt = decode(ws[L["tasks"]:L["tasks"] + 4 * n].view(np.int32))
+    assert np.all(mb < nmb) and np.all(nt < np.where(ph == 1, n2, n1))
+    key = (ph * nmb + mb) * max(n1, n2) + nt
+    assert len(np.unique(key)) == n and np.sum(ph == 0) == nmb * n1
+    pos = np.arange(n)
+    last_l1, first_l2 = np.full(nmb, -1), np.full(nmb, n)
+    np.maximum.at(last_l1, mb[ph == 0], pos[ph == 0])
+    np.minimum.at(first_l2, mb[ph == 1], pos[ph == 1])
+    assert np.all(last_l1 < first_l2), "a Linear-2 tile precedes a Linear-1 tile of its m-block"
+
+    table = {k: ws[L[k]:L[k] + 4 * nmb].view(np.int32) for k in ("mblk_expert", "mblk_row0", "mblk_rows")}
+    recs = ws[L["group_tasks"]:L["group_tasks"] + 16 * int(hdr[40])].view(np.int32).reshape(-1, 4)
+    real = recs[recs[:, 0] != NOP]
+    rph, rmb, rnt = decode(real[:, 0])
+    wide = (table["mblk_rows"] & WIDE) != 0
+    runs = ~(wide[mb] & (nt % 2 == 1))  # tiles the kernel runs: all but odd n-tiles of wide blocks
+    assert len(real) == np.sum(runs)
+    assert np.array_equal(np.sort((rph * nmb + rmb) * max(n1, n2) + rnt), np.sort(key[runs]))
+    assert np.array_equal(real[:, 1], table["mblk_expert"][rmb])
+    assert np.array_equal(real[:, 2], table["mblk_row0"][rmb])
+    assert np.array_equal(real[:, 3], table["mblk_rows"][rmb])
 
 
 @pytest.mark.parametrize("name", ["tiny", "dsv3_share", "qwen3_30b_a3b", "small_m_zipf", "dit_batch"])
@@ -25,13 +76,16 @@ def test_full_size_sampled_parity(name):
     dev = Device(d)
     note("  gpu run (expert-wave order)")
     cfg = make_cfg(s, schedule=moe.MOE_SCHED_EXPERT_WAVE)
-    b = run(cfg, dev)
+    b = run_filled(cfg, dev)
+    check_plan(cfg, b)
     note("  gpu run (interleaved order)")
-    b2 = run(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev)
+    cfg2 = make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED)
+    b2 = run_filled(cfg2, dev)
+    check_plan(cfg2, b2)
     for key in ("act", "yd", "out"):
         assert torch.equal(b[key].view(torch.int16), b2[key].view(torch.int16)), key
     note("  gpu run (interleaved order, dispatch folded into the Linear-1 loads)")
-    b3 = run(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev, gather=True)
+    b3 = run_filled(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev, gather=True)
     for key in ("act", "yd", "out"):
         assert torch.equal(b2[key].view(torch.int16), b3[key].view(torch.int16)), key
     del b3
