@@ -132,9 +132,9 @@ def test_top1_single_expert_matches_dense_ffn():
 
 
 def tie_logits(T, E, k):
-    """Logits full of ties: equal values, -0 against +0, ties between experts e and e + 64
-    (different 64-expert blocks of one lane), and rows where fewer than k logits are finite so
-    that -inf logits are kept (lower ids first, weight 0)."""
+    """Logits full of ties: equal values, -0 against +0, ties between experts e and e + 16,
+    e + 32 and e + 64 (one lane's logits in the 16-, 32- and 64-lane layouts), and rows where
+    fewer than k logits are finite so that -inf logits are kept (lower ids first, weight 0)."""
     lg = np.zeros((T, E), np.float32)
     lg[1::2] = -0.0
     lg[::3, 5 % E] = 1.0
@@ -146,16 +146,18 @@ def tie_logits(T, E, k):
         lg[1::4, E - 1] = 3.0
         lg[1::4, E - 65] = 3.0
         lg[3::8, 64:] = 4.0  # the lower block's ids lose to the higher block's larger logits
+        lg[5::6, [20, 36, 52]] = 2.5
     lg[2::9] = -np.inf
     lg[2::9, : max(1, k // 2)] = np.float32(-1.0)
     return lg
 
 
-@pytest.mark.parametrize("E,k", [(8, 3), (16, 5), (32, 8), (48, 7), (64, 6), (100, 8), (130, 5), (300, 12),
-                                 (1024, 32)])
+@pytest.mark.parametrize("E,k", [(8, 3), (16, 5), (32, 8), (48, 7), (64, 6), (100, 8), (128, 8), (128, 16),
+                                 (72, 32), (112, 17), (130, 5), (300, 12), (1024, 32)])
 def test_routing_ties_and_signed_zero(E, k):
     # equal logits and -0/+0 must pick the lower expert id first, exactly like the oracle; the
-    # shapes cover every route kernel (8- to 64-lane segments, 2 to 5 experts per lane)
+    # shapes cover every route kernel (8- to 64-lane segments, 2 to 16 experts per lane) and
+    # k up to 32 with 2 experts per lane
     T = 128
     lg = tie_logits(T, E, k)
     s = W.shape(T=T, H=64, I=64, E=E, k=k, seed=23)
