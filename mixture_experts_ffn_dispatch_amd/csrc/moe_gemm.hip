@@ -41,6 +41,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
+// cache-policy operand of gfx950 buffer instructions: sc1 (device scope)
+constexpr int kCachePolicySC1 = 16;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -443,7 +445,13 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       if (col < ldim) {  // ldim is a multiple of 64, so a chunk is wholly inside or outside
         for (int r = tid / CPR; r < nrows && r < bm; r += NT / CPR) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + obuf_off(r, c));
-          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, (int)(((uint32_t)(row0 + r) * (uint32_t)ldim + (uint32_t)col) * 2u), 0, 0);
+          const int so = (int)(((uint32_t)(row0 + r) * (uint32_t)ldim + (uint32_t)col) * 2u);
+          // A is read by Linear-2 tiles on any XCD once the m-block is released: device-scope
+          // stores write it through, so the release's L2 write-back has less to do. Yd keeps
+          // the default policy, which leaves much of it in the memory-side cache for the
+          // combine.
+          if (l2) __builtin_amdgcn_raw_buffer_store_b128(v, r_out, so, 0, 0);
+          else __builtin_amdgcn_raw_buffer_store_b128(v, r_out, so, 0, kCachePolicySC1);
         }
       }
     }
