@@ -43,6 +43,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
 // cache-policy operand of gfx950 buffer instructions: sc1 (device scope)
 constexpr int kCachePolicySC1 = 16;
+// Claim result that tells the workgroup to release the completions it holds and claim again:
+// given when its own group's list runs out, so the holds are not kept through the scan of the
+// other groups' cursors (one atomic each). Never a task: m-block 0x7FFFF is out of range.
+constexpr int32_t kFlushTask = 0x7FFFFFFD;
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -140,7 +144,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   // Linear-1 completions are released in batches of kReleaseBatch: one drain of the stores and
   // one agent-scope release (an L2 write-back) for several m-block counters. A workgroup holds
   // completions only while it runs Linear-1 tiles, which never wait; it releases them before
-  // any Linear-2 tile (which may wait) and before it exits, so no wait depends on a held one.
+  // any Linear-2 tile (which may wait), before it exits, and when its own group's list runs
+  // out, so no wait depends on a held one and none outlasts the scan of the other groups.
   // Holding delays a release by up to one Linear-1 tile, which costs nothing only when the
   // Linear-2 tiles that wait for it lie a whole wave later in the list: an interleaved order
   // with a lead of at least two waves. Otherwise every completion is released at once.
@@ -191,6 +196,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
             continue;
           }
           ++scan_group;  // this group's list is used up
+          if (npend > 0) {  // publish held completions before scanning the other groups
+            rec = i32x4{kFlushTask, -1, 0, 0};
+            break;
+          }
         }
       }
       s_task[0] = rec[0];
@@ -203,6 +212,10 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const int task = __builtin_amdgcn_readfirstlane(s_task[0]);
     if (npend > 0 && (task == kNoTask || ((unsigned)task >> kTaskL2Bit) != 0u)) release();
     if (task == kNoTask) break;
+    if (task == kFlushTask) {
+      release();
+      continue;
+    }
     const bool l2 = ((unsigned)task >> kTaskL2Bit) != 0u;
     const int mb = (task >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
     const int nt = task & kTaskNtMask;
