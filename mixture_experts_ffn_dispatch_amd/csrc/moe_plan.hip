@@ -664,7 +664,7 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
   const int R = a.T * a.k;
   const int c0 = chunk * a.chunk_tokens * a.k;
   const int c1 = min(R, c0 + a.chunk_tokens * a.k);
-  const int per_wave = ((c1 - c0 + kPlanWaves - 1) / kPlanWaves + 63) / 64 * 64;
+  const int per_wave = (c1 - c0 + kPlanWaves - 1) / kPlanWaves;  // every wavefront takes a share
   const int f0 = min(c1, c0 + wave * per_wave), f1 = min(c1, f0 + per_wave);
   for (int e = tid; e < a.E; e += kPlanThreads)
     for (int w = 0; w < kPlanWaves; ++w) run[w][e] = 0;
