@@ -85,11 +85,21 @@ def test_auto_tile_height(T, k, E, tile):
     (dict(flags=6), moe.MOE_ERR_INVALID_ARG),  # wide last m-blocks forced both on and off
     (dict(reserved=(0, 1, 0, 0)), moe.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=8192, k=8, E=64), moe.MOE_ERR_UNSUPPORTED),  # row buffers past 4 GiB
+    # 2^24 rows in 32-row tiles: m-block 0x7FFFF would exist, which the sentinel task words
+    # (no task, no-op slot, flush) rely on being out of range
+    (dict(T=1 << 22, k=4, E=64, H=64, I=64, tile_m=32), moe.MOE_ERR_UNSUPPORTED),
 ])
 def test_invalid_configs_rejected(kw, code):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_workspace_size(_cfg(**kw))
     assert ei.value.status == code
+
+
+def test_large_plan_below_the_limits_accepted():
+    # 2^22 rows in 32-row tiles: 131134 m-blocks at most, 262268 tiles, below both limits
+    L = moe.moe_workspace_layout(_cfg(T=1 << 20, k=4, E=64, H=64, I=64, tile_m=32))
+    assert L["max_mblk"] == ((1 << 22) + 64 * 31) // 32 < (1 << 19) - 1
+    assert L["max_tasks"] == 2 * L["max_mblk"] <= 1 << 20
 
 
 def test_null_pointers_rejected_before_any_launch():
