@@ -1,22 +1,28 @@
 """Benchmark: one GPU's share of the expert-parallel MoE FFN layer on MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_share]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dit_batch]
 
 A step is one pass of the whole layer over one batch already resident in HBM: moe_plan
 (route, histogram, scan, scatter, tile list) -> moe_forward_gather (persistent grouped GEMM with
 the dispatch gather folded into the Linear-1 loads: Linear-1 + SwiGLU, Linear-2; or, with
---dispatch separate, moe_dispatch then moe_forward) -> moe_combine. W untimed steps, then
-exactly K timed steps bracketed by device synchronisation, with events only around the forward
-call; the per-call breakdown comes from a separate shorter pass with events between all calls.
-Prints ONE JSON line on stdout.
+--dispatch separate, moe_dispatch then moe_forward) -> moe_combine. The headline workload is
+the largest one (dit_batch: T = 65536, H = 4096, I = 8192, E = 16, k = 2). W untimed steps,
+then exactly K timed steps bracketed by device synchronisation; events on the launch stream
+mark each step and its forward call. Prints ONE JSON line on stdout.
 
-value = layer TFLOP/s = 6*T*k*H*I per step / seconds per step (the two expert GEMMs).
+value = layer TFLOP/s = 6*T*k*H*I per step / wall-clock seconds per step (the two expert GEMMs).
 roofline = the persistent GEMM kernel (the dominant launch): its flops per launch divided by
 its average duration, measured with events on the stream it runs on, against the dense bf16
-MFMA peak of MI355X (2.5 PFLOP/s).
-cpu_baseline = the CPU oracle (float64 NumPy) on a bounded sample of the same workload: the
-first experts' rows (whole experts, in expert order) until about 10 s of work, scaled to
-TFLOP/s by the sample's flops.
+MFMA peak of MI355X (2.5 PFLOP/s); for an HBM-bound workload its algorithmic bytes against
+8 TB/s.
+schedules = both tile orders timed in alternating trials, the order of the pair rotated from
+one trial to the next (X-Stage paper, Section 5, setup: warm up, repeat, report the median,
+rotate the scheduler order): median, min and max microseconds per layer.
+workloads = the same alternating trials for the other named workloads, with the GEMM's
+event-timed duration, its fraction of the MFMA peak, and its algorithmic HBM rate.
+cpu_baseline = the CPU oracle (float64 NumPy) on a bounded sample of the headline workload:
+the first experts' rows (whole experts, in expert order) until about 10 s of work, scaled to
+TFLOP/s by the sample's flops; with the host's CPU model and core counts.
 """
 from __future__ import annotations
 
@@ -121,12 +127,37 @@ def cpu_baseline(s, data, budget_s: float = 10.0) -> dict:
                       f"routing of all {s.T} tokens charged pro rata; {t_total:.1f} s"}
 
 
+def host_cpu() -> dict:
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": usable, "logical_cpus": os.cpu_count()}
+
+
+def stats_us(ms) -> dict:
+    import numpy as np
+
+    a = np.asarray(ms, dtype=float) * 1e3
+    return {"median": round(float(np.median(a)), 2), "min": round(float(a.min()), 2),
+            "max": round(float(a.max()), 2), "n": int(a.size)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="dsv3_share")
+    ap.add_argument("--workload", default="dit_batch")
     ap.add_argument("--schedule", choices=["interleaved", "expert_wave"], default="interleaved")
     ap.add_argument("--lead", type=int, default=0, help="interleave lead D (0 = chosen by the plan)")
     ap.add_argument("--tile-m", type=int, default=0)
@@ -136,7 +167,11 @@ def main() -> int:
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--wide-tails", choices=["auto", "on", "off"], default="auto",
                     help="wide last m-blocks: the library's choice, forced on, or off (comparison)")
+    ap.add_argument("--trials", type=int, default=10,
+                    help="alternating trials per schedule (0 or --no-compare: the headline schedule only)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
+    ap.add_argument("--others", default="tiny,dsv3_share,qwen3_30b_a3b,small_m_zipf",
+                    help="comma-separated workloads measured after the headline ('none': skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--lib", default=None, help="load another build of libmoe (same ABI) instead of the in-tree one")
@@ -159,93 +194,132 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     moe.load(args.lib)
-    s = W.shape(args.workload)
-    log(f"workload {W.describe(s)}")
-    t0 = time.perf_counter()
-    data = W.generate(s)
-    log(f"generated inputs in {time.perf_counter() - t0:.1f} s")
+    stream = torch.cuda.current_stream()
+    sched = {"interleaved": moe.MOE_SCHED_INTERLEAVED, "expert_wave": moe.MOE_SCHED_EXPERT_WAVE}
+    fused = args.dispatch == "fused"
 
     def dev(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
-    x, w1, w2 = dev(data["x"]), dev(data["w1"]), dev(data["w2"])
-    logits = torch.from_numpy(data["logits"]).cuda()
-    sched = {"interleaved": moe.MOE_SCHED_INTERLEAVED, "expert_wave": moe.MOE_SCHED_EXPERT_WAVE}
+    class Layer:
+        """One workload's inputs on the GPU, with the buffers of one schedule."""
 
-    def make_cfg(name):
-        return moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
-                             schedule=sched[name], lead_waves=args.lead, tile_m=args.tile_m,
-                             num_workgroups=args.num_workgroups,
-                             flags={"auto": 0, "on": moe.MOE_FLAG_WIDE_TAILS,
-                                    "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails])
+        def __init__(self, s, inputs, name):
+            self.s, self.name = s, name
+            self.x, self.logits, self.w1, self.w2 = inputs
+            self.cfg = moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
+                                     schedule=sched[name], lead_waves=args.lead, tile_m=args.tile_m,
+                                     num_workgroups=args.num_workgroups,
+                                     flags={"auto": 0, "on": moe.MOE_FLAG_WIDE_TAILS,
+                                            "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails])
+            self.b = moe.alloc_buffers(self.cfg, xd=not fused)
 
-    stream = torch.cuda.current_stream()
+        def step(self, ev=None):
+            """One layer. ev: four events (step start, forward start, forward end, step end), or
+            None; with five events, one between every two calls (breakdown)."""
+            c, b = self.cfg, self.b
+            five = ev is not None and len(ev) == 5
 
-    def timed(name, steps, warmup):
-        cfg = make_cfg(name)
-        fused = args.dispatch == "fused"
-        b = moe.alloc_buffers(cfg, xd=not fused)
-
-        def step(fwd_ev=None, call_ev=None):
-            # fwd_ev: two events around the forward call; call_ev: five events between the calls
             def mark(i):
-                if call_ev is not None:
-                    call_ev[i].record(stream)
+                if ev is not None:
+                    ev[i].record(stream)
 
             mark(0)
-            moe.moe_plan(cfg, logits, b, b["ws"])
-            mark(1)
+            moe.moe_plan(c, self.logits, b, b["ws"])
+            if five:
+                mark(1)
             if not fused:
-                moe.moe_dispatch(cfg, b, x, b["xd"])
-            mark(2)
-            if fwd_ev is not None:
-                fwd_ev[0].record(stream)
+                moe.moe_dispatch(c, b, self.x, b["xd"])
+            mark(2 if five else 1)
             if fused:
-                moe.moe_forward_gather(cfg, b, x, w1, w2, b["act"], b["yd"], b["ws"])
+                moe.moe_forward_gather(c, b, self.x, self.w1, self.w2, b["act"], b["yd"], b["ws"])
             else:
-                moe.moe_forward(cfg, b["xd"], w1, w2, b["act"], b["yd"], b["ws"])
-            if fwd_ev is not None:
-                fwd_ev[1].record(stream)
-            mark(3)
-            moe.moe_combine(cfg, b, b["yd"], b["out"])
-            mark(4)
+                moe.moe_forward(c, b["xd"], self.w1, self.w2, b["act"], b["yd"], b["ws"])
+            mark(3 if five else 2)
+            moe.moe_combine(c, b, b["yd"], b["out"])
+            mark(4 if five else 3)
 
-        for _ in range(warmup):
-            step()
-        st = moe.moe_status_read(b["ws"])
-        assert st == moe.MOE_OK, moe.strerror(st)
-        # Timed region: K whole layers back to back. Only the forward call is bracketed by
-        # events (its mean duration is the roofline's `achieved`); events between every call
-        # would add their own gaps to the step.
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        t_start = time.perf_counter()
-        for i in range(steps):
-            step(fwd_ev=ev[i])
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
-        st = moe.moe_status_read(b["ws"])
-        assert st == moe.MOE_OK, moe.strerror(st)
-        fwd = np.array([e[0].elapsed_time(e[1]) for e in ev])  # ms
-        # per-call breakdown from a separate, shorter pass with events between the calls
-        nb = min(steps, 10)
-        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nb)]
-        for i in range(nb):
-            step(call_ev=evb[i])
-        torch.cuda.synchronize()
-        per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evb])  # ms
-        step_ms = np.array([e[0].elapsed_time(e[4]) for e in evb])
-        counts = b["counts"].cpu().numpy()
-        layout = moe.moe_workspace_layout(cfg)
-        lead_used = int(b["ws"][:128].cpu().numpy().view(np.int32)[HDR_LEAD])
-        return dict(wall_ms=wall * 1e3 / steps, fwd_ms=fwd, step_ms=step_ms, per=per, counts=counts,
-                    layout=layout, lead_used=lead_used)
+        def check(self):
+            st = moe.moe_status_read(self.b["ws"])
+            assert st == moe.MOE_OK, moe.strerror(st)
 
-    main_res = timed(args.schedule, args.steps, args.warmup)
-    other = None
-    if not args.no_compare:
+        def lead_used(self):
+            return int(self.b["ws"][:128].cpu().numpy().view(np.int32)[HDR_LEAD])
+
+    def events(n, m):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(m)] for _ in range(n)]
+
+    def alternate(layers, trials):
+        """Alternating trials: each trial runs every schedule once, the order rotated from one
+        trial to the next. Returns per schedule the layer and forward times (ms)."""
+        ev = {l.name: events(trials, 4) for l in layers}
+        for i in range(trials):
+            for j in range(len(layers)):
+                l = layers[(i + j) % len(layers)]
+                l.step(ev[l.name][i])
+        torch.cuda.synchronize()
+        for l in layers:
+            l.check()
+        return {l.name: (np.array([e[0].elapsed_time(e[3]) for e in ev[l.name]]),
+                         np.array([e[1].elapsed_time(e[2]) for e in ev[l.name]])) for l in layers}
+
+    def load_inputs(name):
+        s = W.shape(name)
+        log(f"workload {W.describe(s)}")
+        t0 = time.perf_counter()
+        data = W.generate(s)
+        inputs = (dev(data["x"]), torch.from_numpy(data["logits"]).cuda(), dev(data["w1"]), dev(data["w2"]))
+        log(f"  inputs generated and uploaded in {time.perf_counter() - t0:.1f} s")
+        return s, data, inputs
+
+    def gemm_roofline(s, counts, fwd_ms):
+        flops = 6.0 * s.T * s.k * s.H * s.I
+        achieved = flops / (fwd_ms * 1e-3) / 1e12
+        gbytes = gemm_bytes(s, counts)
+        gbps = gbytes / (fwd_ms * 1e-3) / 1e9
+        # the GEMM's bound: MFMA when its algorithmic intensity is above the MFMA/HBM ridge
+        # (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), HBM below it (small M: weights dominate)
+        mfma = flops / gbytes >= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+        return mfma, achieved, gbps
+
+    # ---- the headline workload
+    s, data, inputs = load_inputs(args.workload)
+    flops = 6.0 * s.T * s.k * s.H * s.I
+    main_l = Layer(s, inputs, args.schedule)
+    for _ in range(args.warmup):
+        main_l.step()
+    main_l.check()
+    # Timed region: K whole layers back to back, four events per step on the launch stream
+    # (step start, forward start and end, step end).
+    ev = events(args.steps, 4)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        main_l.step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    main_l.check()
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in ev])
+    fwd_ms_all = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    # per-call breakdown from a separate, shorter pass with events between all calls
+    nb = min(args.steps, 10)
+    evb = events(nb, 5)
+    for i in range(nb):
+        main_l.step(evb[i])
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in evb])  # ms
+    counts = main_l.b["counts"].cpu().numpy()
+    layout = moe.moe_workspace_layout(main_l.cfg)
+    lead_used = main_l.lead_used()
+    schedules = None
+    if not args.no_compare and args.trials > 0:
         oname = "expert_wave" if args.schedule == "interleaved" else "interleaved"
-        other = (oname, timed(oname, args.steps, args.warmup))
+        other_l = Layer(s, inputs, oname)
+        for _ in range(args.warmup):
+            other_l.step()
+        res = alternate([main_l, other_l], args.trials)
+        schedules = {n: {"us_per_layer": stats_us(r[0]), "forward_us": stats_us(r[1])} for n, r in res.items()}
+        del other_l
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -253,22 +327,17 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    flops = 6.0 * s.T * s.k * s.H * s.I
-    ms = float(main_res["wall_ms"])
-    fwd_ms = float(np.mean(main_res["fwd_ms"]))
-    counts = main_res["counts"]
+    ms = wall * 1e3 / args.steps
+    fwd_ms = float(np.mean(fwd_ms_all))
     traffic = traffic_from_profiles(args.workload)
-    achieved = flops / (fwd_ms * 1e-3) / 1e12
-    # the GEMM's bound: MFMA when its algorithmic intensity is above the MFMA/HBM ridge
-    # (2.5 PFLOP/s / 8 TB/s = 312.5 flop/B), HBM below it (small M: weights dominate)
-    gbytes = gemm_bytes(s, counts)
-    if flops / gbytes >= MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9):
+    mfma, achieved, gbps = gemm_roofline(s, counts, fwd_ms)
+    if mfma:
         roof = {"bound": "mfma", "kernel": "gemm_persistent_kernel", "achieved": round(achieved, 3),
                 "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic}
     else:
-        gbps = gbytes / (fwd_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "kernel": "gemm_persistent_kernel", "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "tflops": round(achieved, 3)}
@@ -286,28 +355,60 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
-                   "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "dispatch": args.dispatch, "lead_waves": args.lead,
-                   "wide_tails": args.wide_tails,
-                   "lead_used": main_res["lead_used"],
-                   "tile_m": main_res["layout"]["tile_m"], "seed": s.seed},
+                   "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "dispatch": args.dispatch,
+                   "lead_waves": args.lead, "wide_tails": args.wide_tails, "lead_used": lead_used,
+                   "tile_m": layout["tile_m"], "seed": s.seed},
         "roofline": roof,
         "us_per_layer": round(ms * 1e3, 2),
+        "step_us": stats_us(step_ms),
+        "forward_us": stats_us(fwd_ms_all),
         "mfma_frac_layer": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
         "hbm_gbps_algorithmic": round(algorithmic_bytes(s, counts) / (ms * 1e-3) / 1e9, 1),
-        "gemm_hbm_gbps_algorithmic": round(gemm_bytes(s, counts) / (fwd_ms * 1e-3) / 1e9, 1),
-        "per_call_us": {k: round(float(np.mean(main_res["per"][:, j])) * 1e3, 2)
+        "gemm_hbm_gbps_algorithmic": round(gbps, 1),
+        "per_call_us": {k: round(float(np.mean(per[:, j])) * 1e3, 2)
                         for j, k in enumerate(("plan", "dispatch", "forward", "combine"))},
-        "step_us_median": round(float(np.median(main_res["step_ms"])) * 1e3, 2),
         "active_experts": int((counts > 0).sum()),
     }
-    if other is not None:
-        oname, o = other
-        rec["other_schedule"] = {"schedule": oname, "value": round(flops / (o["wall_ms"] * 1e-3) / 1e12, 3),
-                                 "us_per_layer": round(float(o["wall_ms"]) * 1e3, 2),
-                                 "forward_us": round(float(np.mean(o["fwd_ms"])) * 1e3, 2)}
+    if schedules is not None:
+        rec["schedules"] = schedules
+    cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")
-        rec["cpu_baseline"] = cpu_baseline(s, data, args.cpu_budget)
+        cpu = cpu_baseline(s, data, args.cpu_budget)
+        cpu.update(host_cpu())
+    del main_l, inputs, data
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads: alternating trials of both schedules
+    others = [n for n in args.others.split(",") if n and n != "none" and n != args.workload]
+    if others:
+        rec["workloads"] = {}
+    for name in others:
+        so, _, inp = load_inputs(name)
+        names = [args.schedule] if args.no_compare else ["interleaved", "expert_wave"]
+        ls = [Layer(so, inp, n) for n in names]
+        for l in ls:
+            for _ in range(args.warmup):
+                l.step()
+        res = alternate(ls, max(args.trials, 1))
+        c = ls[0].b["counts"].cpu().numpy()
+        lay, fw = res[args.schedule]
+        fmean = float(np.mean(fw))
+        mfma_o, ach, gb = gemm_roofline(so, c, fmean)
+        fl = 6.0 * so.T * so.k * so.H * so.I
+        w = {"bound": "mfma" if mfma_o else "hbm", "us_per_layer": stats_us(lay),
+             "tflops": round(fl / (float(np.median(lay)) * 1e-3) / 1e12, 2),
+             "gemm_us": round(fmean * 1e3, 2), "gemm_tflops": round(ach, 2),
+             "gemm_mfma_frac": round(ach / MFMA_PEAK_TFLOPS, 4),
+             "gemm_hbm_gbps": round(gb, 1), "gemm_hbm_frac": round(gb / HBM_PEAK_GBPS, 4),
+             "lead_used": ls[0].lead_used(), "tile_m": moe.moe_workspace_layout(ls[0].cfg)["tile_m"]}
+        if len(ls) > 1:
+            w["expert_wave_us_per_layer"] = stats_us(res["expert_wave"][0])
+        rec["workloads"][name] = w
+        del ls, inp
+        torch.cuda.empty_cache()
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -288,9 +288,20 @@ __device__ inline int step_min(int v, int* s_tmp) {
   if constexpr (ONE) return wave_min(v);
   else return block_min(v, s_tmp);
 }
+// Publishes LDS writes of the wave-table step to the other lanes (ONE: the lanes of
+// wavefront 0 exchange values through LDS, e.g. lane i writes a[i] and lane i - D reads it).
+// The fences order the LDS accesses at wavefront scope, so the compiler may not move a later
+// load of another lane's entry above this lane's store, and the wave barrier keeps the
+// scheduler from moving code across.
 template <bool ONE>
 __device__ inline void step_sync() {
-  if constexpr (!ONE) __syncthreads();
+  if constexpr (ONE) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+    __syncthreads();
+  }
 }
 
 // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
@@ -385,6 +396,7 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
     // interleaved: L1(0) .. L1(D-1), then segment i = L2(i) merged with L1(i + D)
     int prefix_total, prefix_units, unused, seg_units;
     const bool lead = tid < min(D, nw);
+    step_sync<ONE>();  // t.a of every wave (written above) is read across lanes below
     const int p = step_scan<ONE>(lead ? aw : 0, s_tmp, prefix_total);
     const int pu = step_scan<ONE>(lead ? auw : 0, s_tmp, prefix_units);
     const int a_next = tid + D < nw ? t.a[tid + D] : 0;

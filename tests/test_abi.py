@@ -95,6 +95,23 @@ def test_invalid_configs_rejected(kw, code):
     assert ei.value.status == code
 
 
+def test_mblock_limit_alone_rejects():
+    # 4193800 * 4 rows in 32-row tiles over 64 experts: at most (16775200 + 64 * 31) / 32 =
+    # 524287 = 0x7FFFF m-blocks, the sentinel task words' m-block, while the tile list
+    # (2 * 524287 = 1048574 tiles) stays below its own limit of 2^20: only the m-block check
+    # can reject this plan
+    kw = dict(T=4193800, k=4, E=64, H=64, I=64, tile_m=32)
+    R = kw["T"] * kw["k"]
+    max_mblk = (R + kw["E"] * (kw["tile_m"] - 1)) // kw["tile_m"]
+    assert max_mblk == 0x7FFFF and 2 * max_mblk <= 1 << 20
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_workspace_size(_cfg(**kw))
+    assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+    # one m-block fewer is accepted
+    L = moe.moe_workspace_layout(_cfg(**dict(kw, T=4193800 - 8)))
+    assert L["max_mblk"] == 0x7FFFF - 1
+
+
 def test_large_plan_below_the_limits_accepted():
     # 2^22 rows in 32-row tiles: 131134 m-blocks at most, 262268 tiles, below both limits
     L = moe.moe_workspace_layout(_cfg(T=1 << 20, k=4, E=64, H=64, I=64, tile_m=32))
