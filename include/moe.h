@@ -20,7 +20,8 @@
  *   - bfloat16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
  *   - Every pointer except `cfg`, `rt` and `bytes`/`layout` outputs is a DEVICE pointer owned
  *     by the caller (for example a torch tensor's data_ptr()). The library never allocates,
- *     frees or retains caller memory and keeps no global state between calls.
+ *     frees or retains caller memory and keeps no global state between calls, apart from the
+ *     static workspace array of moe_layer_noalloc and its per-device address.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every device call
  *     is asynchronous on that stream and performs no host synchronisation, except
  *     moe_status_read, which synchronises the stream.
@@ -232,6 +233,30 @@ moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, cons
  *   yd [T*k, H] bf16 in; out [T, H] bf16 out. */
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd,
                        uint16_t* out, void* stream);
+
+/* ---- Layer without caller-provided workspace ----
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. moe_layer_noalloc runs moe_plan, moe_forward_gather
+ * and moe_combine (the same kernels, so the same bytes) with the workspace in a static device
+ * array of MOE_STATIC_WORKSPACE_BYTES inside the library instead of a caller buffer. It calls
+ * no hipMalloc, hipFree or other allocating routine. Each GPU the library runs on holds its own
+ * array until the process ends; its device address is looked up with hipGetSymbolAddress on
+ * the first call on that device (made with that device current) and kept.
+ *   logits, rt, x, w1, w2, act, yd, out: as for moe_plan / moe_forward_gather / moe_combine
+ *     (caller-owned device buffers; rt's arrays are written).
+ *   status: device int32 or NULL; receives the device-side error word (MOE_OK or
+ *     MOE_ERR_TIMEOUT, as moe_status_read reports it) by a 4-byte device-to-device copy
+ *     ordered after the layer on `stream`.
+ * Every call on one GPU shares that GPU's array, and each call's moe_plan rewrites every part
+ * of it that the later kernels read: calls on one GPU must be ordered (one stream, or events);
+ * calls that overlap on one GPU race and give undefined results.
+ * Errors: as moe_plan; MOE_ERR_WORKSPACE when moe_workspace_size(cfg) exceeds
+ * MOE_STATIC_WORKSPACE_BYTES (checked before anything is launched); MOE_ERR_HIP if the array's
+ * address cannot be obtained or a launch fails. */
+#define MOE_STATIC_WORKSPACE_BYTES (8u << 20)
+moe_status moe_layer_noalloc(const moe_config* cfg, const float* logits, const moe_routing* rt,
+                             const uint16_t* x, const uint16_t* w1, const uint16_t* w2, uint16_t* act,
+                             uint16_t* yd, uint16_t* out, int32_t* status, void* stream);
 
 /* ---- Burst-Gap calibration (X-Stage paper, Section 3: the Burst-Gap microbenchmarks) ----
  * K producers each store a burst of B bytes, then compute for a gap G, for P periods; the

@@ -26,6 +26,7 @@ MOE_SCHED_INTERLEAVED = 1
 MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
 MOE_FLAG_NO_WIDE_TAILS = 0x2
 MOE_FLAG_WIDE_TAILS = 0x4
+MOE_STATIC_WORKSPACE_BYTES = 8 << 20  # workspace array of moe_layer_noalloc
 
 
 class MoeError(RuntimeError):
@@ -112,6 +113,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                                 vp]),
         "moe_combine": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
         "moe_status_read": (ctypes.c_int32, [vp, ctypes.c_size_t, vp]),
+        "moe_layer_noalloc": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, vp, vp, vp, vp, vp, vp, vp]),
         "moe_burst_gap": (ctypes.c_int32, [P(CBurstCfg), vp, ctypes.c_size_t, vp, vp]),
         "moe_burst_clock_hz": (ctypes.c_int32, [P(ctypes.c_int64)]),
     }
@@ -210,6 +212,15 @@ def moe_forward_gather(cfg, rt: dict, x, w1, w2, act, yd, ws, stream=None) -> No
 def moe_combine(cfg, rt: dict, yd, out, stream=None) -> None:
     _check(load().moe_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(yd), _ptr(out),
                               _stream(stream)), "moe_combine")
+
+
+def moe_layer_noalloc(cfg, logits, rt: dict, x, w1, w2, act, yd, out, status=None, stream=None) -> None:
+    """The whole layer (plan, forward with the gather, combine) with the library's static
+    workspace array; ``status`` (a device int32 tensor or None) receives the device-side error
+    word."""
+    _check(load().moe_layer_noalloc(ctypes.byref(_cfg(cfg)), _ptr(logits), ctypes.byref(_routing(rt)), _ptr(x),
+                                    _ptr(w1), _ptr(w2), _ptr(act), _ptr(yd), _ptr(out), _ptr(status),
+                                    _stream(stream)), "moe_layer_noalloc")
 
 
 def moe_burst_gap(producers: int, nbytes: int, periods: int, gap_ticks: int, buf, times, stream=None) -> None:

@@ -2,7 +2,14 @@
 // kernel launches. Host code only; every call validates before it launches anything.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
+
+// The workspace of moe_layer_noalloc: one array per GPU, held until the process ends. In host
+// code this name is only a stand-in for the symbol; its device address comes from
+// hipGetSymbolAddress (scratch_address below), and only that address is used.
+static __device__ __align__(256) unsigned char scratch[MOE_STATIC_WORKSPACE_BYTES];
 
 namespace moe {
 namespace {
@@ -170,8 +177,9 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
   return st;
 }
 
-moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
-                    size_t ws_bytes, void* stream) {
+namespace {
+moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
+                     size_t ws_bytes, void* stream) {
   moe_ws_layout L;
   moe_status st = compute_layout(cfg, &L);
   if (st != MOE_OK) return st;
@@ -220,6 +228,12 @@ moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routin
   if (launch_scan_schedule(a, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_scatter(a, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
+                    size_t ws_bytes, void* stream) {
+  return plan_impl(cfg, logits, rt, ws, ws_bytes, stream);
 }
 
 moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint16_t* x, uint16_t* xd,
@@ -288,6 +302,54 @@ moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, cons
                               void* stream) {
   if (!rt || !rt->perm || !x) return MOE_ERR_INVALID_ARG;
   return forward_impl(cfg, nullptr, x, rt->perm, w1, w2, act, yd, ws, ws_bytes, stream);
+}
+
+namespace {
+// Device address of this GPU's scratch array, looked up once per device (with that device
+// current) and kept; later calls on the device reuse it.
+moe_status scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_layer_noalloc(const moe_config* cfg, const float* logits, const moe_routing* rt,
+                             const uint16_t* x, const uint16_t* w1, const uint16_t* w2, uint16_t* act,
+                             uint16_t* yd, uint16_t* out, int32_t* status, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if (L.total_bytes > (size_t)MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+  if (!logits || !rt || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm || !rt->pos ||
+      !x || !w1 || !w2 || !act || !yd || !out)
+    return MOE_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MOE_OK) return st;
+  // moe_plan initialises every part of the workspace the later kernels read (header, cursors,
+  // dependency counters, tile lists), so the array's contents from an earlier call do not
+  // matter; the GEMM's last workgroup resets its counters again on exit
+  if ((st = plan_impl(cfg, logits, rt, ws, MOE_STATIC_WORKSPACE_BYTES, stream)) != MOE_OK) return st;
+  if ((st = forward_impl(cfg, nullptr, x, rt->perm, w1, w2, act, yd, ws, MOE_STATIC_WORKSPACE_BYTES, stream)) !=
+      MOE_OK)
+    return st;
+  if ((st = moe_combine(cfg, rt, yd, out, stream)) != MOE_OK) return st;
+  // the device-side error word (header slot 0) for the caller, a 4-byte device-to-device copy
+  if (status && hipMemcpyAsync(status, at<int32_t>(ws, L.header) + HDR_ERROR, sizeof(int32_t),
+                               hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd, uint16_t* out,
