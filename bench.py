@@ -177,6 +177,9 @@ def main() -> int:
     ap.add_argument("--lib", default=None, help="load another build of libmoe (same ABI) instead of the in-tree one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--trace-summary", default=None,
+                    help="also run one traced layer per schedule of the headline workload and write "
+                         "its per-tile phases to this file")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -320,6 +323,29 @@ def main() -> int:
         res = alternate([main_l, other_l], args.trials)
         schedules = {n: {"us_per_layer": stats_us(r[0]), "forward_us": stats_us(r[1])} for n, r in res.items()}
         del other_l
+
+    if args.trace_summary:
+        from mixture_experts_ffn_dispatch_amd import tracing
+
+        hz = moe.moe_burst_clock_hz()
+        text = [f"# command: python3 bench.py {' '.join(sys.argv[1:])}",
+                "# per-tile phases of gemm_persistent_kernel from its trace (one traced layer per schedule, "
+                "after the timed runs)"]
+        for name in ("interleaved", "expert_wave"):
+            tl = Layer(s, inputs, name)
+            tl.step()
+            buf = torch.full((layout["max_slots"] * 64,), 0xFF, dtype=torch.uint8, device="cuda")
+            tl.cfg.trace = buf
+            tl.step()
+            tl.cfg.trace = None
+            torch.cuda.synchronize()
+            tl.check()
+            ph = tracing.tile_phases(buf.cpu().numpy().view(moe._lib.TRACE_DTYPE), hz)
+            text.append(tracing.format_phases(f"{s.name} {name} (lead {tl.lead_used()})", ph))
+            del tl, buf
+        with open(args.trace_summary, "w") as f:
+            f.write("\n".join(text) + "\n")
+        log("\n".join(text))
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Status codes. */
 typedef enum {
@@ -94,8 +94,34 @@ typedef struct moe_config {
   int32_t tile_m;           /* rows per GEMM tile: 0 = chosen from T*k/E, else 32, 64, 128, 256 */
   int32_t spin_limit;       /* bounded-wait iterations of a Linear-2 tile; 0 = default (~seconds)*/
   int32_t flags;            /* must be 0 except MOE_FLAG_* bits below                            */
-  int32_t reserved[4];      /* must be 0                                                         */
+  int32_t reserved[2];      /* must be 0                                                         */
+  void* trace;              /* per-tile trace of moe_forward (moe_trace_rec below), NULL = off   */
 } moe_config;
+
+/* Per-tile trace (X-Stage paper, Section 5: per-tile instrumentation of the persistent kernel to
+ * check which tile order ran and where its time went). When moe_config.trace is not NULL,
+ * moe_forward / moe_forward_gather / moe_layer_noalloc write one record per tile they run into
+ * that device buffer, which must hold moe_ws_layout.max_slots records. Record i belongs to
+ * record slot i of the locality groups' tile lists (moe_ws_layout.group_tasks), or, when the
+ * grid has fewer than 8 workgroups (one shared cursor), to list position i of the tile list.
+ * Slots no tile ran (no-op slots, the odd n-tiles of wide m-blocks) are left untouched, so
+ * callers fill the buffer with a marker first. Times are readings of the constant-rate
+ * real-time counter (frequency: moe_burst_clock_hz), taken by the workgroup's waves in step;
+ * records are written by one lane with vector stores at the end of each tile. With trace NULL
+ * the kernel takes none of these readings. Results never depend on the trace. */
+typedef struct moe_trace_rec {
+  int32_t task;       /* task word (bit 31 Linear-2, bits 30..12 m-block, bits 11..0 n-tile)      */
+  int32_t workgroup;  /* persistent workgroup (block index) that ran the tile                     */
+  int32_t xcc;        /* XCC (XCD) it ran on (hardware register XCC_ID)                           */
+  int32_t hw_id;      /* raw HW_ID register of its first wavefront (CU, shader engine, SIMD)      */
+  int64_t t_claim;    /* before the claim (one atomic on the group cursor, then the record load) */
+  int64_t t_claimed;  /* the tile's record in hand                                               */
+  int64_t t_start;    /* main loop starts (Linear-2: after its dependency wait)                   */
+  int64_t t_epilogue; /* main loop done, epilogue starts                                         */
+  int64_t t_end;      /* epilogue stores issued                                                  */
+  int64_t t_release;  /* Linear-1: its completion released (after the agent-scope release fence,
+                         before the m-block counter is bumped); Linear-2: 0                      */
+} moe_trace_rec;
 
 /* Test hook: make every Linear-2 tile wait for one Linear-1 completion that never comes, so the
    bounded wait expires (after spin_limit iterations) and the kernel exits normally with
@@ -250,6 +276,8 @@ moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint1
  * Every call on one GPU shares that GPU's array, and each call's moe_plan rewrites every part
  * of it that the later kernels read: calls on one GPU must be ordered (one stream, or events);
  * calls that overlap on one GPU race and give undefined results.
+ * cfg->trace must be NULL (MOE_ERR_INVALID_ARG otherwise): the traced kernel instances are a
+ * measurement aid and may use private memory.
  * Errors: as moe_plan; MOE_ERR_WORKSPACE when moe_workspace_size(cfg) exceeds
  * MOE_STATIC_WORKSPACE_BYTES (checked before anything is launched); MOE_ERR_HIP if the array's
  * address cannot be obtained or a launch fails. */

@@ -12,7 +12,7 @@ from dataclasses import dataclass, field
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
-ABI_VERSION = 3  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
+ABI_VERSION = 4  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -38,7 +38,7 @@ class MoeError(RuntimeError):
 class CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "H", "I", "E", "k", "experts_per_wave", "schedule", "lead_waves", "num_workgroups",
-        "tile_m", "spin_limit", "flags")] + [("reserved", ctypes.c_int32 * 4)]
+        "tile_m", "spin_limit", "flags")] + [("reserved", ctypes.c_int32 * 2), ("trace", ctypes.c_void_p)]
 
 
 class CRouting(ctypes.Structure):
@@ -51,6 +51,17 @@ class CLayout(ctypes.Structure):
         "tasks", "unit_start", "group_units", "group_tasks", "wave_table")] + [(n, ctypes.c_int32) for n in (
             "chunks", "chunk_tokens", "max_mblk", "max_tasks", "max_slots", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
             "n2_tiles")]
+
+
+class CTraceRec(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("task", "workgroup", "xcc", "hw_id")] + [
+        (n, ctypes.c_int64) for n in ("t_claim", "t_claimed", "t_start", "t_epilogue", "t_end", "t_release")]
+
+
+# numpy view of a trace buffer (moe_trace_rec, 64 bytes per record)
+TRACE_DTYPE = [("task", "<i4"), ("workgroup", "<i4"), ("xcc", "<i4"), ("hw_id", "<i4"), ("t_claim", "<i8"),
+               ("t_claimed", "<i8"), ("t_start", "<i8"), ("t_epilogue", "<i8"), ("t_end", "<i8"),
+               ("t_release", "<i8")]
 
 
 class CBurstCfg(ctypes.Structure):
@@ -74,7 +85,8 @@ class MoeConfig:
     tile_m: int = 0
     spin_limit: int = 0
     flags: int = 0
-    reserved: tuple = field(default=(0, 0, 0, 0))
+    reserved: tuple = field(default=(0, 0))
+    trace: object = None  # device buffer of moe_trace_rec (a torch tensor or an address), or None
 
     def to_c(self) -> CConfig:
         c = CConfig()
@@ -83,6 +95,7 @@ class MoeConfig:
             setattr(c, n, int(getattr(self, n)))
         for i, v in enumerate(self.reserved):
             c.reserved[i] = int(v)
+        c.trace = _ptr(self.trace)
         return c
 
 

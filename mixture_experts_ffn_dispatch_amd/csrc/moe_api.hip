@@ -36,7 +36,7 @@ moe_status check_config(const moe_config* c) {
   if (c->lead_waves < 0 || c->num_workgroups < 0 || c->spin_limit < 0) return MOE_ERR_INVALID_ARG;
   if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_NO_WIDE_TAILS) && (c->flags & MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
     if (c->reserved[i] != 0) return MOE_ERR_INVALID_ARG;
   if (c->tile_m != 0 && c->tile_m != 32 && c->tile_m != 64 && c->tile_m != 128 && c->tile_m != 256)
     return MOE_ERR_UNSUPPORTED;
@@ -285,6 +285,7 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_
   g.max_mblk = L.max_mblk;
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
+  g.trace = static_cast<moe_trace_rec*>(cfg->trace);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_gemm(g, L.tile_m, plan_wide_tails(cfg, L.tile_m), cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
@@ -332,6 +333,8 @@ moe_status moe_layer_noalloc(const moe_config* cfg, const float* logits, const m
   moe_status st = compute_layout(cfg, &L);
   if (st != MOE_OK) return st;
   if (L.total_bytes > (size_t)MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_WORKSPACE;
+  // the traced GEMM instances are a measurement aid and may use private (scratch) memory
+  if (cfg->trace) return MOE_ERR_INVALID_ARG;
   if (!logits || !rt || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm || !rt->pos ||
       !x || !w1 || !w2 || !act || !yd || !out)
     return MOE_ERR_INVALID_ARG;

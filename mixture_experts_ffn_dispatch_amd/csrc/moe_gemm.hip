@@ -29,6 +29,9 @@
 //    never change a result bit.
 //  * Loads and stores use buffer resources bounded to the m-block's rows and the expert's
 //    weight slab: rows past the end read as zero and are never stored.
+//  * With a trace buffer, every tile's claim, wait, main loop, epilogue and release are
+//    timed with the real-time counter (Section 5 of the paper instruments its kernel per tile
+//    the same way); without one, none of it runs.
 #include "moe_internal.h"
 
 namespace moe {
@@ -47,6 +50,19 @@ constexpr int kCachePolicySC1 = 16;
 // given when its own group's list runs out, so the holds are not kept through the scan of the
 // other groups' cursors (one atomic each). Never a task: m-block 0x7FFFF is out of range.
 constexpr int32_t kFlushTask = 0x7FFFFFFD;
+
+// The constant-rate real-time counter (its frequency is the device's wall-clock rate).
+__device__ inline long long rt_clock() { return (long long)__builtin_amdgcn_s_memrealtime(); }
+__device__ inline int hw_xcc_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & 0xFu);
+}
+__device__ inline int hw_id() {
+  unsigned v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(v));
+  return (int)v;
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
@@ -95,7 +111,7 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW, bool WIDE>
+template <int BM, int WN, int WM, int MINW, bool WIDE, bool TRACE>
 __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
@@ -119,10 +135,13 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   static_assert(!WIDE_OK || (LD == LDN + BM / RG + 2 && (BM / 2) % RG == 0), "wide staging");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  // The tile record and the exit flag live at the start of LDS stage 1: that stage is first
-  // written only after a barrier that every wave passes after reading the record.
+  // The tile record, its trace slot and the exit flag live at the start of LDS stage 1: that
+  // stage is first written only after a barrier that every wave passes after reading them.
   int* const s_task = reinterpret_cast<int*>(&lds[STAGE]);
-  int* const s_last = s_task + 4;
+  int* const s_last = s_task + 5;
+  // per-tile trace: only the TRACE instances (launched when a trace buffer is given) hold
+  // any of its code, so the others are unchanged by it
+  constexpr bool tracing = TRACE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, LDS chunk slot
@@ -152,6 +171,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   const int batch = p.hdr[HDR_LEAD] >= 2 ? kReleaseBatch : 1;
   int npend = 0;                     // completions held (the same value in every lane)
   int pend_mb[kReleaseBatch] = {};  // thread 0: their m-blocks
+  int pend_slot[kReleaseBatch] = {};  // thread 0: their trace records
   auto release = [&]() {
     // every wavefront drains its own stores first (a workgroup barrier alone does not wait
     // for them), then one lane releases at agent scope and bumps the counters
@@ -159,6 +179,12 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     __syncthreads();
     if (tid == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if constexpr (tracing) {
+        const long long t = rt_clock();
+#pragma unroll
+        for (int i = 0; i < kReleaseBatch; ++i)
+          if (i < npend) p.trace[pend_slot[i]].t_release = t;
+      }
 #pragma unroll
       for (int i = 0; i < kReleaseBatch; ++i)
         if (i < npend) __hip_atomic_fetch_add(&p.mb_ready[pend_mb[i]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -166,13 +192,17 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     npend = 0;
   };
   for (;;) {
+    long long t_claim = 0;
+    if constexpr (tracing) t_claim = rt_clock();
     if (tid == 0) {
       i32x4 rec = {kNoTask, -1, 0, 0};  // task word, expert, first row, rows
+      int slot = -1;                    // its trace record: the list position or record slot
       if (p.ngroups == 1) {
         const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
         for (;;) {
           const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
           if (t < 0 || t >= ntasks) break;
+          slot = t;
           rec[0] = p.tasks[t];
           const int mb = (rec[0] >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
           if (mb < p.max_mblk) {  // the m-block record is read only for an index inside the table
@@ -190,6 +220,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
           const int i = atomicAdd(&p.hdr[HDR_GROUP_CURSOR + g], 1);
           const int lo = max(p.hdr[HDR_GTASK_OFF + g], 0), hi = min(p.hdr[HDR_GTASK_OFF + g + 1], p.max_slots);
           if (i >= 0 && i < hi - lo) {
+            slot = lo + i;
             rec = *reinterpret_cast<const i32x4*>(p.gtasks + 4 * (size_t)(lo + i));
             if (rec[0] != kNopTask) break;
             rec = i32x4{kNoTask, -1, 0, 0};  // a spare slot: claim again
@@ -206,8 +237,11 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       s_task[1] = rec[1];
       s_task[2] = rec[2];
       s_task[3] = rec[3];
+      if constexpr (tracing) s_task[4] = slot;
     }
     __syncthreads();
+    long long t_claimed = 0;
+    if constexpr (tracing) t_claimed = rt_clock();
     // the task and its m-block record are the same for the whole workgroup: keep them scalar
     const int task = __builtin_amdgcn_readfirstlane(s_task[0]);
     if (npend > 0 && (task == kNoTask || ((unsigned)task >> kTaskL2Bit) != 0u)) release();
@@ -222,6 +256,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     const int e = __builtin_amdgcn_readfirstlane(s_task[1]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_task[2]);
     const int rows_word = __builtin_amdgcn_readfirstlane(s_task[3]);
+    const int slot = tracing ? __builtin_amdgcn_readfirstlane(s_task[4]) : -1;
     const bool wide = WIDE_OK && (rows_word & kRowsWide) != 0;
     const int nrows = rows_word & ~kRowsWide;
     // a plan this workspace could not have produced: skip the tile, report, never fault
@@ -255,6 +290,15 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
+    }
+    if (tracing && tid == 0 && (unsigned)slot < (unsigned)p.max_slots) {
+      // the record's head now, its tail after the epilogue: no reading is kept through the
+      // main loop (one lane, vector stores)
+      moe_trace_rec* const r = &p.trace[slot];
+      *reinterpret_cast<i32x4*>(&r->task) = i32x4{task, (int)blockIdx.x, hw_xcc_id(), hw_id()};
+      r->t_claim = t_claim;
+      r->t_claimed = t_claimed;
+      r->t_start = rt_clock();
     }
 
     // operand buffers bounded to this expert's weight slab and this m-block's rows
@@ -406,6 +450,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     }
     if (kt < KT) step(0, kt);
     __syncthreads();  // the epilogue's next task reuses both stages
+    if (tracing && tid == 0 && (unsigned)slot < (unsigned)p.max_slots) p.trace[slot].t_epilogue = rt_clock();
 
     // Epilogue through LDS (both stages are free after the mainloop's last barrier), so that
     // global stores cover whole row segments instead of 8 bytes of 32 rows per instruction.
@@ -469,11 +514,19 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
       }
     }
 
+    if (tracing && tid == 0 && (unsigned)slot < (unsigned)p.max_slots) {
+      // the record's tail (a Linear-1 tile's release time follows when it is released)
+      p.trace[slot].t_end = rt_clock();
+      p.trace[slot].t_release = 0;
+    }
     if (!l2) {  // hold this tile's completion; release when the batch is full
       if (tid == 0) {
 #pragma unroll
         for (int i = 0; i < kReleaseBatch; ++i)
-          if (i == npend) pend_mb[i] = mb;
+          if (i == npend) {
+            pend_mb[i] = mb;
+            pend_slot[i] = (unsigned)slot < (unsigned)p.max_slots ? slot : 0;
+          }
       }
       if (++npend >= batch) release();
     }
@@ -500,7 +553,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
 
 template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t variant_grid(int num_workgroups, int* grid) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE>;
+  // the traced instance has the same resources' limits: the grid is sized on the plain one
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -518,7 +572,8 @@ hipError_t variant_grid(int num_workgroups, int* grid) {
 
 template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE>;
+  auto kern = a.trace ? gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, true>
+                      : gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false>;
   constexpr int NT = 64 * WN * WM;
   int grid = 0;
   hipError_t err = variant_grid<BM, WN, WM, MINW, WIDE>(num_workgroups, &grid);

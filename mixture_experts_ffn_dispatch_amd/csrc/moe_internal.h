@@ -128,6 +128,7 @@ struct GemmArgs {
   int max_slots;            // capacity of the group record lists
   int spin_limit;
   int force_timeout;
+  moe_trace_rec* trace;  // per-tile records (moe_config.trace), or null
 };
 
 // Launchers (return the hipError_t of the launch).

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.abi_version() == 3
+    assert moe.abi_version() == 4
 
 
 
@@ -34,9 +34,19 @@ def test_binding_matches_header():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     assert int(re.search(r"#define MOE_ABI_VERSION (\d+)", text).group(1)) == _lib.ABI_VERSION
     for struct, cls in (("moe_config", _lib.CConfig), ("moe_routing", _lib.CRouting),
-                        ("moe_ws_layout", _lib.CLayout), ("moe_burst_cfg", _lib.CBurstCfg)):
+                        ("moe_ws_layout", _lib.CLayout), ("moe_burst_cfg", _lib.CBurstCfg),
+                        ("moe_trace_rec", _lib.CTraceRec)):
         body = re.search(r"typedef struct " + struct + r" \{(.*?)\} " + struct + ";", text, flags=re.S).group(1)
         assert re.findall(r"(\w+)(?:\[\d+\])?;", body) == [n for n, _ in cls._fields_], struct
+
+
+def test_struct_sizes():
+    # moe_config keeps 64 bytes (the trace pointer took two reserved words), and a trace
+    # record is 64 bytes, matching the numpy view the tests read traces with
+    import numpy as np
+
+    assert ctypes.sizeof(_lib.CConfig) == 64 and _lib.CConfig.trace.offset == 56
+    assert ctypes.sizeof(_lib.CTraceRec) == 64 == np.dtype(_lib.TRACE_DTYPE).itemsize
 
 
 def test_strerror():
@@ -83,7 +93,7 @@ def test_auto_tile_height(T, k, E, tile):
     (dict(tile_m=48), moe.MOE_ERR_UNSUPPORTED),
     (dict(flags=8), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=6), moe.MOE_ERR_INVALID_ARG),  # wide last m-blocks forced both on and off
-    (dict(reserved=(0, 1, 0, 0)), moe.MOE_ERR_INVALID_ARG),
+    (dict(reserved=(0, 1)), moe.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=8192, k=8, E=64), moe.MOE_ERR_UNSUPPORTED),  # row buffers past 4 GiB
     # 2^24 rows in 32-row tiles: m-block 0x7FFFF would exist, which the sentinel task words
     # (no task, no-op slot, flush) rely on being out of range

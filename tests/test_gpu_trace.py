@@ -1,0 +1,121 @@
+"""The per-tile trace (moe_config.trace): one record per tile the persistent kernel runs, in
+the tile's record slot, with ordered real-time readings; it shows which order ran (the
+dependency, the XCD of each workgroup, claims in list order) and never changes a result."""
+import numpy as np
+import pytest
+import torch
+
+import moe_workloads as W
+from tests.gpu_util import Device, fetch, make_cfg, note, run
+
+import mixture_experts_ffn_dispatch_amd as moe
+from mixture_experts_ffn_dispatch_amd import _lib
+
+pytestmark = pytest.mark.gpu
+
+NOP = 0x7FFFFFFE
+
+
+def traced(cfg, dev, gather=True):
+    L = moe.moe_workspace_layout(cfg)
+    buf = torch.full((L["max_slots"] * 64,), 0xFF, dtype=torch.uint8, device="cuda")  # task = -1
+    cfg.trace = buf
+    b = run(cfg, dev, gather=gather)
+    cfg.trace = None
+    return b, buf.cpu().numpy().view(_lib.TRACE_DTYPE), L
+
+
+def plan_records(b, L):
+    ws = b["ws"].cpu().numpy()
+    hdr = ws[:256].view(np.int32)
+    nslots = int(hdr[40])  # end of the last group's record list
+    recs = ws[L["group_tasks"]:L["group_tasks"] + 16 * nslots].view(np.int32).reshape(-1, 4)
+    goff = hdr[32:41].astype(np.int64)
+    return recs, goff, hdr
+
+
+def decode(task):
+    w = np.asarray(task, np.int64) & 0xFFFFFFFF
+    return w >> 31, (w >> 12) & 0x7FFFF, w & 0xFFF
+
+
+def check_trace(tr, recs, goff, hdr):
+    n = len(recs)
+    ran = tr[:n]
+    runs = recs[:, 0] != NOP  # the group lists hold no-op records for the odd n-tiles of wide m-blocks
+    # one record per tile the kernel ran, in its slot; no-op slots untouched; nothing past the lists
+    assert np.array_equal(ran["task"][runs], recs[runs, 0])
+    assert np.all(ran["task"][~runs] == -1)
+    assert np.all(tr["task"][n:] == -1)
+    r = ran[runs]
+    ph, mb, _ = decode(r["task"])
+    # readings in order inside every record
+    assert np.all(r["t_claim"] <= r["t_claimed"]) and np.all(r["t_claimed"] <= r["t_start"])
+    assert np.all(r["t_start"] <= r["t_epilogue"]) and np.all(r["t_epilogue"] <= r["t_end"])
+    l1, l2 = ph == 0, ph == 1
+    assert np.all(r["t_release"][l1] >= r["t_end"][l1]) and np.all(r["t_release"][l2] == 0)
+    # no Linear-2 tile starts before the last release of its m-block's Linear-1 tiles
+    last_rel = np.zeros(int(hdr[3]), np.int64)
+    np.maximum.at(last_rel, mb[l1], r["t_release"][l1])
+    assert np.all(r["t_start"][l2] >= last_rel[mb[l2]]), "a Linear-2 tile started before its rows were released"
+    # workgroup w runs on XCD w % 8: its locality group is the XCD whose L2 it shares
+    assert np.array_equal(r["xcc"], r["workgroup"] % 8)
+    # each workgroup takes the records of one group list in list order
+    slots = np.flatnonzero(runs)
+    group = np.searchsorted(goff, slots, side="right") - 1
+    for wg in np.unique(r["workgroup"]):
+        sel = r["workgroup"] == wg
+        order = np.argsort(r["t_claim"][sel], kind="stable")
+        g, sl = group[sel][order], slots[sel][order]
+        for gg in np.unique(g):
+            assert np.all(np.diff(sl[g == gg]) > 0), f"workgroup {wg} took group {gg}'s records out of order"
+    return r, ph, mb
+
+
+@pytest.mark.parametrize("name,schedule", [
+    ("dsv3_share", moe.MOE_SCHED_INTERLEAVED), ("dsv3_share", moe.MOE_SCHED_EXPERT_WAVE),
+    ("qwen3_30b_a3b", moe.MOE_SCHED_INTERLEAVED), ("small_m_zipf", moe.MOE_SCHED_INTERLEAVED),
+    ("tiny", moe.MOE_SCHED_INTERLEAVED)])
+def test_trace_records_every_tile_in_order(name, schedule):
+    s = W.shape(name)
+    note(f"trace: {W.describe(s)} schedule {schedule}")
+    dev = Device(W.generate(s))
+    cfg = make_cfg(s, schedule=schedule)
+    b, tr, L = traced(cfg, dev)
+    recs, goff, hdr = plan_records(b, L)
+    r, ph, mb = check_trace(tr, recs, goff, hdr)
+    # the trace changes nothing: same bytes as an untraced run
+    ref = run(make_cfg(s, schedule=schedule), dev, gather=True)
+    for key in ("act", "yd", "out"):
+        assert torch.equal(b[key].view(torch.int16), ref[key].view(torch.int16)), key
+    note(f"  {len(r)} tiles traced on {len(np.unique(r['workgroup']))} workgroups")
+
+
+def test_interleaved_order_runs_later_linear1_between_linear2_tiles():
+    # dsv3_share with lead 1: the Linear-1 tiles of wave i + 1 are claimed while wave i's
+    # Linear-2 tiles are still being claimed; in the Expert-Wave order every group claims all
+    # of wave i's Linear-2 tiles of its list before any Linear-1 tile of wave i + 1
+    s = W.shape("dsv3_share")
+    dev = Device(W.generate(s))
+    waves = s.waves
+    res = {}
+    for schedule in (moe.MOE_SCHED_INTERLEAVED, moe.MOE_SCHED_EXPERT_WAVE):
+        cfg = make_cfg(s, schedule=schedule, lead_waves=1 if schedule == moe.MOE_SCHED_INTERLEAVED else 0)
+        b, tr, L = traced(cfg, dev)
+        recs, goff, hdr = plan_records(b, L)
+        r, ph, mb = check_trace(tr, recs, goff, hdr)
+        table = b["ws"].cpu().numpy()[L["mblk_expert"]:L["mblk_expert"] + 4 * int(hdr[3])].view(np.int32)
+        wave = table[mb] // s.experts_per_wave
+        res[schedule] = (r, ph, wave)
+    r, ph, wave = res[moe.MOE_SCHED_INTERLEAVED]
+    for i in range(waves - 1):
+        l2_last = r["t_claimed"][(ph == 1) & (wave == i)].max()
+        l2_first = r["t_claimed"][(ph == 1) & (wave == i)].min()
+        l1_next = r["t_claimed"][(ph == 0) & (wave == i + 1)]
+        inside = np.mean((l1_next > l2_first) & (l1_next < l2_last))
+        assert inside > 0.5, f"wave {i}: only {inside:.0%} of the next wave's Linear-1 tiles ran among its Linear-2 tiles"
+    r, ph, wave = res[moe.MOE_SCHED_EXPERT_WAVE]
+    for i in range(waves - 1):
+        l2_first = r["t_claimed"][(ph == 1) & (wave == i)].min()
+        l1_next = r["t_claimed"][(ph == 0) & (wave == i + 1)]
+        assert np.mean(l1_next > l2_first) > 0.95
