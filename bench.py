@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 HBM_PEAK_GBPS = 8000.0
 HDR_LEAD = 26  # workspace header slot holding the interleave lead the plan used
+HDR_SCHED = 28  # ... and the order it wrote (0 Expert-Wave, 1 interleaved)
 
 
 def log(*a):
@@ -158,7 +159,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="dit_batch")
-    ap.add_argument("--schedule", choices=["interleaved", "expert_wave"], default="interleaved")
+    ap.add_argument("--schedule", choices=["auto", "interleaved", "expert_wave"], default="auto",
+                    help="tile order of the headline: auto (moe_plan picks order and lead), interleaved "
+                         "(lead --lead, 0 = D_knee), expert_wave")
     ap.add_argument("--lead", type=int, default=0, help="interleave lead D (0 = chosen by the plan)")
     ap.add_argument("--tile-m", type=int, default=0)
     ap.add_argument("--dispatch", choices=["fused", "separate"], default="fused",
@@ -198,7 +201,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     moe.load(args.lib)
     stream = torch.cuda.current_stream()
-    sched = {"interleaved": moe.MOE_SCHED_INTERLEAVED, "expert_wave": moe.MOE_SCHED_EXPERT_WAVE}
+    sched = {"auto": moe.MOE_SCHED_AUTO, "interleaved": moe.MOE_SCHED_INTERLEAVED,
+             "expert_wave": moe.MOE_SCHED_EXPERT_WAVE}
     fused = args.dispatch == "fused"
 
     def dev(a):
@@ -211,7 +215,8 @@ def main() -> int:
             self.s, self.name = s, name
             self.x, self.logits, self.w1, self.w2 = inputs
             self.cfg = moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
-                                     schedule=sched[name], lead_waves=args.lead, tile_m=args.tile_m,
+                                     schedule=sched[name], lead_waves=0 if name == "auto" else args.lead,
+                                     tile_m=args.tile_m,
                                      num_workgroups=args.num_workgroups,
                                      flags={"auto": 0, "on": moe.MOE_FLAG_WIDE_TAILS,
                                             "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails])
@@ -248,6 +253,9 @@ def main() -> int:
 
         def lead_used(self):
             return int(self.b["ws"][:128].cpu().numpy().view(np.int32)[HDR_LEAD])
+
+        def order_used(self):
+            return ["expert_wave", "interleaved"][int(self.b["ws"][:128].cpu().numpy().view(np.int32)[HDR_SCHED])]
 
     def events(n, m):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(m)] for _ in range(n)]
@@ -314,15 +322,19 @@ def main() -> int:
     counts = main_l.b["counts"].cpu().numpy()
     layout = moe.moe_workspace_layout(main_l.cfg)
     lead_used = main_l.lead_used()
+    order_used = main_l.order_used()
     schedules = None
     if not args.no_compare and args.trials > 0:
-        oname = "expert_wave" if args.schedule == "interleaved" else "interleaved"
-        other_l = Layer(s, inputs, oname)
-        for _ in range(args.warmup):
-            other_l.step()
-        res = alternate([main_l, other_l], args.trials)
+        others_l = [Layer(s, inputs, n) for n in ("auto", "interleaved", "expert_wave") if n != args.schedule]
+        for l in others_l:
+            for _ in range(args.warmup):
+                l.step()
+        res = alternate([main_l] + others_l, args.trials)
         schedules = {n: {"us_per_layer": stats_us(r[0]), "forward_us": stats_us(r[1])} for n, r in res.items()}
-        del other_l
+        for l in [main_l] + others_l:
+            schedules[l.name]["order"] = l.order_used()
+            schedules[l.name]["lead"] = l.lead_used()
+        del others_l
 
     if args.trace_summary:
         from mixture_experts_ffn_dispatch_amd import tracing
@@ -331,7 +343,7 @@ def main() -> int:
         text = [f"# command: python3 bench.py {' '.join(sys.argv[1:])}",
                 "# per-tile phases of gemm_persistent_kernel from its trace (one traced layer per schedule, "
                 "after the timed runs)"]
-        for name in ("interleaved", "expert_wave"):
+        for name in ("auto", "interleaved", "expert_wave"):
             tl = Layer(s, inputs, name)
             tl.step()
             buf = torch.full((layout["max_slots"] * 64,), 0xFF, dtype=torch.uint8, device="cuda")
@@ -341,7 +353,7 @@ def main() -> int:
             torch.cuda.synchronize()
             tl.check()
             ph = tracing.tile_phases(buf.cpu().numpy().view(moe._lib.TRACE_DTYPE), hz)
-            text.append(tracing.format_phases(f"{s.name} {name} (lead {tl.lead_used()})", ph))
+            text.append(tracing.format_phases(f"{s.name} {name} ({tl.order_used()}, lead {tl.lead_used()})", ph))
             del tl, buf
         with open(args.trace_summary, "w") as f:
             f.write("\n".join(text) + "\n")
@@ -382,7 +394,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "dispatch": args.dispatch,
-                   "lead_waves": args.lead, "wide_tails": args.wide_tails, "lead_used": lead_used,
+                   "lead_waves": args.lead, "wide_tails": args.wide_tails, "order_used": order_used,
+                   "lead_used": lead_used,
                    "tile_m": layout["tile_m"], "seed": s.seed},
         "roofline": roof,
         "us_per_layer": round(ms * 1e3, 2),
@@ -411,7 +424,8 @@ def main() -> int:
         rec["workloads"] = {}
     for name in others:
         so, _, inp = load_inputs(name)
-        names = [args.schedule] if args.no_compare else ["interleaved", "expert_wave"]
+        names = [args.schedule] if args.no_compare else \
+            [args.schedule] + [n for n in ("auto", "interleaved", "expert_wave") if n != args.schedule]
         ls = [Layer(so, inp, n) for n in names]
         for l in ls:
             for _ in range(args.warmup):
@@ -427,9 +441,11 @@ def main() -> int:
              "gemm_us": round(fmean * 1e3, 2), "gemm_tflops": round(ach, 2),
              "gemm_mfma_frac": round(ach / MFMA_PEAK_TFLOPS, 4),
              "gemm_hbm_gbps": round(gb, 1), "gemm_hbm_frac": round(gb / HBM_PEAK_GBPS, 4),
-             "lead_used": ls[0].lead_used(), "tile_m": moe.moe_workspace_layout(ls[0].cfg)["tile_m"]}
-        if len(ls) > 1:
-            w["expert_wave_us_per_layer"] = stats_us(res["expert_wave"][0])
+             "order_used": ls[0].order_used(), "lead_used": ls[0].lead_used(),
+             "tile_m": moe.moe_workspace_layout(ls[0].cfg)["tile_m"]}
+        for l in ls[1:]:
+            w[f"{l.name}_us_per_layer"] = stats_us(res[l.name][0])
+            w[f"{l.name}_lead"] = l.lead_used()
         rec["workloads"][name] = w
         del ls, inp
         torch.cuda.empty_cache()

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Status codes. */
 typedef enum {
@@ -63,8 +63,37 @@ enum {
      the Linear-2 tiles of wave w (X-Stage paper, Section 4.1 "reshape injection" and Section
      4.2 on MegaMoE: ready Linear-1 work of later waves is moved between Linear-2 epilogues;
      the lead is the dependency-derived threshold the paper calls D_knee). */
-  MOE_SCHED_INTERLEAVED = 1
+  MOE_SCHED_INTERLEAVED = 1,
+  /* moe_plan picks the order and the lead itself, from the routed tile counts and the X-Stage
+     calibration in moe_config (X-Stage paper, Discussion, burst-shaping paragraph: a runtime
+     compares the predicted X-Stage stall reduction with the locality cost and selects the
+     original or the interleaved schedule for the current routing and working set). The rule
+     is stated below; lead_waves must be 0. The choice is recorded in the workspace header. */
+  MOE_SCHED_AUTO = 2
 };
+
+/* The MOE_SCHED_AUTO rule. Per expert wave i: a_i Linear-1 and b_i Linear-2 tiles, A_i bytes of
+   activation (rows x I x 2); G persistent workgroups; tile height BM. A tile's main loop over
+   K is estimated as t(K) = G * max(2 BM 256 K / P, 512 K / B) (P = 1.2e15 flop/s and
+   B = 5.0e12 B/s, the kernel's sustained MFMA and weight-streaming rates on this GPU);
+   t1 = t(H), t2 = t(I). Candidates: Expert-Wave, and interleaved with lead D = 1 .. waves. For
+   each wave with Linear-2 tiles:
+     aligned producers K = max(1, min(G, b_i) * s), s = b_i t2 / (b_i t2 + a_{i+D} t1) the
+             Linear-2 share of the work when wave i + D's Linear-1 tiles are spread among wave
+             i's Linear-2 tiles (s = 1 in the Expert-Wave order; a_{i+D} = 0 past the last wave),
+     burst   V = K * BM * 256 * 2 bytes (their Yd stores, Section 4.2: V = K_act V_t),
+     gap     g = t2 (each producer's Linear-2 main loop between its bursts),
+     issue   T = max(t_iss0, V / R - g), and at least (V - Q) / R when V - R t_iss0 > Q
+             (the max law and the capacity bound of Section 3),
+     X-Stage stall   += (b_i / K) * (T - t_iss0),
+     dependency stall += t1 / 2 when the wave's Linear-2 tiles can be reached before its
+             Linear-1 tiles are done: always in the Expert-Wave order, and in the interleaved
+             order when dist_i(D) * (A H + B I) < G * H * (A + B) (the lead rule above).
+   Locality cost: the activation bytes kept live while wave i's Linear-2 tiles run (A_i, or
+   A_i + ... + A_{i+D} interleaved) above 256 MiB (the last-level cache), the worst wave, divided
+   by B, counted only when the GEMM's algorithmic bytes / B exceed its flops / P. The candidate
+   with the smallest stall + dependency stall + locality cost wins; ties go to interleaved and
+   then to the larger lead. Computed in double precision without fused multiply-adds. */
 
 /* Lead chosen by moe_plan when lead_waves is 0 (interleaved order): a Linear-2 tile of wave w
    should be taken only after the last Linear-1 tile of wave w has finished. With G persistent
@@ -89,12 +118,18 @@ typedef struct moe_config {
   int32_t k;                /* experts per token (1..min(E, 32))                                 */
   int32_t experts_per_wave; /* W >= 1; wave w holds experts [w*W, min(E, (w+1)*W))              */
   int32_t schedule;         /* MOE_SCHED_*                                                       */
-  int32_t lead_waves;       /* interleaved order only: D >= 1, or 0 = chosen by moe_plan (below) */
+  int32_t lead_waves;       /* interleaved order only: D >= 1, or 0 = chosen by moe_plan (below);
+                               0 with MOE_SCHED_AUTO                                             */
   int32_t num_workgroups;   /* persistent grid; 0 or more than fits at once = every resident slot */
   int32_t tile_m;           /* rows per GEMM tile: 0 = chosen from T*k/E, else 32, 64, 128, 256 */
   int32_t spin_limit;       /* bounded-wait iterations of a Linear-2 tile; 0 = default (~seconds)*/
   int32_t flags;            /* must be 0 except MOE_FLAG_* bits below                            */
-  int32_t reserved[2];      /* must be 0                                                         */
+  /* X-Stage calibration of the path the Linear-2 stores take, for MOE_SCHED_AUTO (0 = this
+     GPU's own memory, as calibrated by moe_burst_gap: 0.927 us, 6646 GB/s, 31.2 MiB) */
+  float xs_issue_us;        /* t_iss0: backpressure-free issue time of a burst, microseconds     */
+  float xs_drain_gbps;      /* R: effective drain rate, GB/s                                    */
+  float xs_capacity_mib;    /* Q: effective outstanding capacity, MiB                           */
+  int32_t reserved;         /* must be 0                                                         */
   void* trace;              /* per-tile trace of moe_forward (moe_trace_rec below), NULL = off   */
 } moe_config;
 
@@ -158,7 +193,9 @@ typedef struct moe_ws_layout {
                            [6] L2 n-tiles per m-block, [7] exited workgroups,
                            [8..15] records handed out from each locality group's list,
                            [16] units in the unit table, [17..25] group unit lists,
-                           [26] interleave lead used, [27] GEMM grid the plan assumed,
+                           [26] interleave lead used (0: Expert-Wave order), [27] GEMM grid
+                           the plan assumed, [28] the order used (MOE_SCHED_EXPERT_WAVE or
+                           MOE_SCHED_INTERLEAVED),
                            [32..40] group record lists (first record of group g, 9th = end) */
   size_t chunk_counts;  /* int32[E * ((chunks + 3) & ~3)]: per-(expert, token chunk) counts, then each
                            chunk's first row among its expert's rows */

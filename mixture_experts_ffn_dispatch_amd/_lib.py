@@ -8,11 +8,11 @@ from __future__ import annotations
 
 import ctypes
 import os
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
-ABI_VERSION = 4  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
+ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -23,6 +23,7 @@ MOE_ERR_TIMEOUT = -5
 
 MOE_SCHED_EXPERT_WAVE = 0
 MOE_SCHED_INTERLEAVED = 1
+MOE_SCHED_AUTO = 2
 MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
 MOE_FLAG_NO_WIDE_TAILS = 0x2
 MOE_FLAG_WIDE_TAILS = 0x4
@@ -38,7 +39,8 @@ class MoeError(RuntimeError):
 class CConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "H", "I", "E", "k", "experts_per_wave", "schedule", "lead_waves", "num_workgroups",
-        "tile_m", "spin_limit", "flags")] + [("reserved", ctypes.c_int32 * 2), ("trace", ctypes.c_void_p)]
+        "tile_m", "spin_limit", "flags")] + [(n, ctypes.c_float) for n in (
+            "xs_issue_us", "xs_drain_gbps", "xs_capacity_mib")] + [("reserved", ctypes.c_int32), ("trace", ctypes.c_void_p)]
 
 
 class CRouting(ctypes.Structure):
@@ -85,7 +87,10 @@ class MoeConfig:
     tile_m: int = 0
     spin_limit: int = 0
     flags: int = 0
-    reserved: tuple = field(default=(0, 0))
+    xs_issue_us: float = 0.0      # X-Stage calibration for MOE_SCHED_AUTO (0 = this GPU's memory)
+    xs_drain_gbps: float = 0.0
+    xs_capacity_mib: float = 0.0
+    reserved: int = 0
     trace: object = None  # device buffer of moe_trace_rec (a torch tensor or an address), or None
 
     def to_c(self) -> CConfig:
@@ -93,8 +98,9 @@ class MoeConfig:
         for n in ("T", "H", "I", "E", "k", "experts_per_wave", "schedule", "lead_waves", "num_workgroups",
                   "tile_m", "spin_limit", "flags"):
             setattr(c, n, int(getattr(self, n)))
-        for i, v in enumerate(self.reserved):
-            c.reserved[i] = int(v)
+        for n in ("xs_issue_us", "xs_drain_gbps", "xs_capacity_mib"):
+            setattr(c, n, float(getattr(self, n)))
+        c.reserved = int(self.reserved)
         c.trace = _ptr(self.trace)
         return c
 

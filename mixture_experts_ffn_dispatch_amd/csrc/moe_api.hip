@@ -32,12 +32,17 @@ moe_status check_config(const moe_config* c) {
   if (!c) return MOE_ERR_INVALID_ARG;
   if (c->T < 1 || c->H < 1 || c->I < 1 || c->E < 1 || c->k < 1 || c->k > c->E) return MOE_ERR_INVALID_ARG;
   if (c->experts_per_wave < 1) return MOE_ERR_INVALID_ARG;
-  if (c->schedule != MOE_SCHED_EXPERT_WAVE && c->schedule != MOE_SCHED_INTERLEAVED) return MOE_ERR_INVALID_ARG;
+  if (c->schedule != MOE_SCHED_EXPERT_WAVE && c->schedule != MOE_SCHED_INTERLEAVED && c->schedule != MOE_SCHED_AUTO)
+    return MOE_ERR_INVALID_ARG;
   if (c->lead_waves < 0 || c->num_workgroups < 0 || c->spin_limit < 0) return MOE_ERR_INVALID_ARG;
+  if (c->schedule == MOE_SCHED_AUTO && c->lead_waves != 0) return MOE_ERR_INVALID_ARG;
+  // calibration: finite and not negative (0 = the local calibration); !(x >= 0) also catches NaN
+  if (!(c->xs_issue_us >= 0.f) || !(c->xs_drain_gbps >= 0.f) || !(c->xs_capacity_mib >= 0.f) ||
+      c->xs_issue_us > 1e9f || c->xs_drain_gbps > 1e9f || c->xs_capacity_mib > 1e9f)
+    return MOE_ERR_INVALID_ARG;
   if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_NO_WIDE_TAILS) && (c->flags & MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
-  for (int i = 0; i < 2; ++i)
-    if (c->reserved[i] != 0) return MOE_ERR_INVALID_ARG;
+  if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
   if (c->tile_m != 0 && c->tile_m != 32 && c->tile_m != 64 && c->tile_m != 128 && c->tile_m != 256)
     return MOE_ERR_UNSUPPORTED;
   if (c->E > MOE_MAX_EXPERTS || c->k > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
@@ -222,6 +227,9 @@ moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routi
   a.H = cfg->H;
   a.I = cfg->I;
   a.wide_tails = plan_wide_tails(cfg, L.tile_m) ? 1 : 0;
+  a.xs_issue_s = (cfg->xs_issue_us > 0.f ? (double)cfg->xs_issue_us : kLocalIssueUs) * 1e-6;
+  a.xs_drain_bps = (cfg->xs_drain_gbps > 0.f ? (double)cfg->xs_drain_gbps : kLocalDrainGBps) * 1e9;
+  a.xs_capacity_b = (cfg->xs_capacity_mib > 0.f ? (double)cfg->xs_capacity_mib : kLocalCapacityMiB) * 1048576.0;
   if (gemm_grid(L.tile_m, a.wide_tails != 0, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;

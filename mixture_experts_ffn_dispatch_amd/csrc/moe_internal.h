@@ -25,12 +25,14 @@ enum : int {
   HDR_GROUP_OFF = 17,     // [17, 26): first entry of each group's unit list (9th = end)
   HDR_LEAD = 26,          // interleave lead the plan used (0 for the Expert-Wave order)
   HDR_PLAN_GRID = 27,     // GEMM grid size the plan assumed when it chose the lead
+  HDR_SCHED = 28,         // the order the plan wrote (MOE_SCHED_EXPERT_WAVE / _INTERLEAVED)
   HDR_GTASK_OFF = 32,     // [32, 41): first record of each group's tile list (9th = end)
   HDR_SLOTS = 64
 };
 
-// Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, which is
-// the XCD it runs on (the hardware deals workgroups to the 8 XCDs round-robin). The list is
+// Locality groups of the persistent GEMM: workgroup w belongs to group w % kGroups, and all
+// workgroups of a group run on one XCD (the hardware deals workgroups to the 8 XCDs
+// round-robin; which XCD gets group 0 varies from one dispatch to the next). The list is
 // made of units (kUnit consecutive tiles of one run, written in blocks of kBlockM m-blocks x
 // kBlockN n-tiles of one expert). Linear-1 units are dealt round-robin to the groups in list
 // order, and so are Linear-2 units, so every group gets an even share of both kinds of work;
@@ -46,6 +48,16 @@ constexpr int kBlockN = 8;
 // expert's first m-block and first row): a head of kWaveTableHead ints, then at most
 // 10 (E + 1) entries.
 constexpr int kWaveTableHead = 24;
+
+// MOE_SCHED_AUTO's model of this kernel on this GPU: sustained MFMA rate of its tiles,
+// weight-streaming rate, the last-level cache, and the local memory path's calibration
+// (moe_burst_gap on this GPU's own memory).
+constexpr double kAutoMfmaFlops = 1.2e15;
+constexpr double kAutoStreamBytes = 5.0e12;
+constexpr double kAutoCacheBytes = 256.0 * 1024 * 1024;
+constexpr double kLocalIssueUs = 0.927;
+constexpr double kLocalDrainGBps = 6646.0;
+constexpr double kLocalCapacityMiB = 31.2;
 
 constexpr int kTileN2 = 256;         // Linear-2 tile: Yd columns
 constexpr int kTileN1 = 128;         // Linear-1 tile: A columns (=> 128 gate + 128 up weight rows)
@@ -101,6 +113,7 @@ struct PlanArgs {
   int tile_m, n1, n2;
   int H, I;      // Linear-1 K = H, Linear-2 K = I (tile durations scale with them)
   int grid;      // persistent GEMM workgroups (tiles in flight)
+  double xs_issue_s, xs_drain_bps, xs_capacity_b;  // X-Stage calibration for MOE_SCHED_AUTO
   int wide_tails;  // 1: m-blocks of at most tile_m / 2 rows become wide (256-row tiles only)
 };
 

@@ -241,7 +241,7 @@ __device__ int block_min(int v, int* s_tmp) {
 // (the scalars below and the group offsets), then eight arrays of nw + 1 entries indexed by
 // expert wave, then the first m-block of each expert (E + 1 entries, the last = all m-blocks)
 // and the expert offsets (E + 1 entries, the last = T k).
-enum : int { kWtLead = 0, kWtL1Units = 1, kWtL2Units = 2, kWtUnits = 3, kWtGoff = 8 };
+enum : int { kWtLead = 0, kWtL1Units = 1, kWtL2Units = 2, kWtUnits = 3, kWtInterleaved = 4, kWtGoff = 8 };
 static_assert(kWtGoff + kGroups + 1 <= kWaveTableHead, "wave table head");
 struct WaveTable {
   int* head;
@@ -304,14 +304,59 @@ __device__ inline void step_sync() {
   }
 }
 
+// Predicted cost (seconds) of one candidate order of the MOE_SCHED_AUTO rule (include/moe.h):
+// D = 0 is the Expert-Wave order, D >= 1 the interleaved order with lead D. Needs the tile
+// counts (t.a, t.b), their prefix sums (t.p1, t.p2, totals A and B), the expert offsets (t.off)
+// and whether the GEMM is HBM-bound. The same double-precision steps as the rule's statement,
+// without fused multiply-adds, so a host model can reproduce the choice exactly.
+__device__ double auto_cost(const PlanArgs& a, const WaveTable& t, int nw, int D, long long A, long long B,
+                            bool hbm_bound) {
+#pragma clang fp contract(off)
+  const double G = (double)a.grid, BM = (double)a.tile_m;
+  const double t1 = G * fmax(2.0 * BM * 256.0 * (double)a.H / kAutoMfmaFlops, 512.0 * (double)a.H / kAutoStreamBytes);
+  const double t2 = G * fmax(2.0 * BM * 256.0 * (double)a.I / kAutoMfmaFlops, 512.0 * (double)a.I / kAutoStreamBytes);
+  const double vt = BM * 256.0 * 2.0;
+  const double R = a.xs_drain_bps, T0 = a.xs_issue_s, Q = a.xs_capacity_b;
+  const long long den = A * a.H + B * a.I;
+  const long long need = (long long)a.grid * a.H * (A + B);
+  double xs = 0.0, dep = 0.0, over = 0.0;
+  for (int i = 0; i < nw; ++i) {
+    // activation bytes live while wave i's Linear-2 tiles run: waves i .. i + D
+    const int last = D > 0 ? min(i + D, nw - 1) : i;
+    const double ws = (double)(t.off[min(a.E, (last + 1) * a.W)] - t.off[i * a.W]) * (double)a.I * 2.0;
+    over = fmax(over, ws - kAutoCacheBytes);
+    const int b = t.b[i];
+    if (b == 0) continue;
+    // the producers whose Linear-2 boundaries align: those on Linear-2 tiles at a time, the
+    // Linear-2 share of the segment's work when Linear-1 tiles of wave i + D are spread in it
+    const int an = (D > 0 && i + D < nw) ? t.a[i + D] : 0;
+    const double share = ((double)b * t2) / ((double)b * t2 + (double)an * t1);
+    const double kact = fmax(1.0, (double)min(a.grid, b) * share);
+    const double V = kact * vt;
+    const double g = t2;
+    double T = fmax(T0, V / R - g);
+    if (V - R * T0 > Q) T = fmax(T, (V - Q) / R);
+    xs += ((double)b / kact) * (T - T0);
+    bool reach = true;
+    if (D > 0) {
+      const long long dist =
+          (long long)t.p2[i] - t.p2[max(0, i - D + 1)] + t.p1[min(i + D, nw)] - t.p1[min(i + 1, nw)];
+      reach = dist * den < need;
+    }
+    if (reach) dep += t1 / 2.0;
+  }
+  return xs + dep + (hbm_bound ? over / kAutoStreamBytes : 0.0);
+}
+
 // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
 //    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
 //    last unit may be shorter); the orders are defined on units, so every unit is one
 //    contiguous stretch of the list holding tiles of a single run. Thread i handles wave i.
 template <bool ONE>
-__device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, int* s_tmp) {
+__device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, int* s_tmp, double* s_cost) {
   const int tid = threadIdx.x, E = a.E, W = a.W;
-  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  const bool automatic = a.schedule == MOE_SCHED_AUTO;
   int aw = 0, bw = 0;
   if (tid < nw) {
     const int m = t.mb[min(E, (tid + 1) * W)] - t.mb[tid * W];
@@ -338,7 +383,7 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
     int A, B;
     const int pa = step_scan<ONE>(aw, s_tmp, A);
     const int pb = step_scan<ONE>(bw, s_tmp, B);
-    if (interleaved && D == 0) {
+    if ((interleaved && D == 0) || automatic) {
       if (tid < nw) {
         t.p1[tid] = pa;
         t.p2[tid] = pb;
@@ -363,6 +408,28 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
         if (ok) cand = Dc;
       }
       D = step_min<ONE>(cand, s_tmp);
+    }
+    if (automatic) {
+      // MOE_SCHED_AUTO: thread t prices the interleaved order with lead t + 1; every thread
+      // prices the Expert-Wave order and reads all prices, so all take the same choice
+      long long rows = t.off[E], active = 0;
+      for (int e = 0; e < E; ++e) active += t.off[e + 1] > t.off[e] ? 1 : 0;
+      const double flops = 6.0 * (double)rows * (double)a.H * (double)a.I;
+      const double bytes = (double)rows * (double)a.H * 4.0 + (double)active * 6.0 * (double)a.H * (double)a.I +
+                           (double)rows * (double)a.I * 4.0;
+      const bool hbm_bound = bytes / kAutoStreamBytes > flops / kAutoMfmaFlops;
+      if (tid < nw) s_cost[tid] = auto_cost(a, t, nw, tid + 1, A, B, hbm_bound);
+      const double ew = auto_cost(a, t, nw, 0, A, B, hbm_bound);
+      step_sync<ONE>();
+      double best = s_cost[0];
+      int bestD = 1;
+      for (int d = 1; d < nw; ++d)
+        if (s_cost[d] <= best) {  // ties go to the larger lead
+          best = s_cost[d];
+          bestD = d + 1;
+        }
+      interleaved = !(ew < best);  // ties go to the interleaved order
+      D = bestD;
     }
     D = min(max(D, 1), max(nw, 1));
   }
@@ -428,6 +495,7 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
   }
   if (tid == 0) {
     t.head[kWtLead] = D;
+    t.head[kWtInterleaved] = interleaved ? 1 : 0;
     t.head[kWtL1Units] = n_l1_units;
     t.head[kWtL2Units] = n_l2_units;
     t.head[kWtUnits] = total_units;
@@ -438,6 +506,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
   __shared__ int s_tmp[32];
   __shared__ int s_cnt[MOE_MAX_EXPERTS];      // rows routed to each expert
   __shared__ int s_tab[kWaveTableHead + 10 * (MOE_MAX_EXPERTS + 1)];  // the wave table
+  __shared__ double s_cost[MOE_MAX_EXPERTS];  // MOE_SCHED_AUTO: price of each interleave lead
   const int tid = threadIdx.x;
   const int E = a.E, BM = a.tile_m;
   const int nw = (E + a.W - 1) / a.W;
@@ -520,9 +589,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
 
   // 3. on wavefront 0 alone when it can (the common case: a few expert waves)
   if (nw <= 64) {
-    if (tid < 64) schedule_waves<true>(a, t, nw, s_tmp);
+    if (tid < 64) schedule_waves<true>(a, t, nw, s_tmp, s_cost);
   } else {
-    schedule_waves<false>(a, t, nw, s_tmp);
+    schedule_waves<false>(a, t, nw, s_tmp, s_cost);
   }
   __syncthreads();
 
@@ -546,7 +615,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
     a.hdr[HDR_N2] = a.n2;
     a.hdr[HDR_DONE] = 0;
     a.hdr[HDR_NUNITS] = total_units;
-    a.hdr[HDR_LEAD] = a.schedule == MOE_SCHED_INTERLEAVED ? t.head[kWtLead] : 0;
+    a.hdr[HDR_LEAD] = t.head[kWtInterleaved] ? t.head[kWtLead] : 0;
+    a.hdr[HDR_SCHED] = t.head[kWtInterleaved] ? MOE_SCHED_INTERLEAVED : MOE_SCHED_EXPERT_WAVE;
     a.hdr[HDR_PLAN_GRID] = a.grid;
   }
 }
@@ -564,7 +634,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_schedule_kernel(PlanArgs a)
 __device__ void place_tile(const PlanArgs& a, const WaveTable& t, int nw, int ph, int mb, int nt) {
   const int n = ph ? a.n2 : a.n1;
   const int BM = a.tile_m, D = t.head[kWtLead];
-  const bool interleaved = a.schedule == MOE_SCHED_INTERLEAVED;
+  const bool interleaved = t.head[kWtInterleaved] != 0;
   int e = 0;  // the expert e with t.mb[e] <= mb < t.mb[e + 1] (the last of equal starts)
   for (int hi = a.E - 1; e < hi;) {
     const int mid = (e + hi + 1) >> 1;

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.abi_version() == 4
+    assert moe.abi_version() == 5
 
 
 
@@ -41,11 +41,12 @@ def test_binding_matches_header():
 
 
 def test_struct_sizes():
-    # moe_config keeps 64 bytes (the trace pointer took two reserved words), and a trace
-    # record is 64 bytes, matching the numpy view the tests read traces with
+    # moe_config: 12 ints, the three X-Stage calibration floats, a reserved word, then the
+    # trace pointer at byte 64; a trace record is 64 bytes, matching the numpy view the tests
+    # read traces with
     import numpy as np
 
-    assert ctypes.sizeof(_lib.CConfig) == 64 and _lib.CConfig.trace.offset == 56
+    assert ctypes.sizeof(_lib.CConfig) == 72 and _lib.CConfig.trace.offset == 64
     assert ctypes.sizeof(_lib.CTraceRec) == 64 == np.dtype(_lib.TRACE_DTYPE).itemsize
 
 
@@ -88,12 +89,16 @@ def test_auto_tile_height(T, k, E, tile):
     (dict(H=100), moe.MOE_ERR_UNSUPPORTED),
     (dict(I=96), moe.MOE_ERR_UNSUPPORTED),
     (dict(experts_per_wave=0), moe.MOE_ERR_INVALID_ARG),
-    (dict(schedule=2), moe.MOE_ERR_INVALID_ARG),
     (dict(lead_waves=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(tile_m=48), moe.MOE_ERR_UNSUPPORTED),
     (dict(flags=8), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=6), moe.MOE_ERR_INVALID_ARG),  # wide last m-blocks forced both on and off
-    (dict(reserved=(0, 1)), moe.MOE_ERR_INVALID_ARG),
+    (dict(reserved=1), moe.MOE_ERR_INVALID_ARG),
+    (dict(schedule=3), moe.MOE_ERR_INVALID_ARG),
+    (dict(schedule=2, lead_waves=2), moe.MOE_ERR_INVALID_ARG),  # the automatic order picks the lead
+    (dict(xs_drain_gbps=-1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(xs_issue_us=float("nan")), moe.MOE_ERR_INVALID_ARG),
+    (dict(xs_capacity_mib=float("inf")), moe.MOE_ERR_INVALID_ARG),
     (dict(T=1 << 20, H=8192, k=8, E=64), moe.MOE_ERR_UNSUPPORTED),  # row buffers past 4 GiB
     # 2^24 rows in 32-row tiles: m-block 0x7FFFF would exist, which the sentinel task words
     # (no task, no-op slot, flush) rely on being out of range

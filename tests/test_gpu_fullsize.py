@@ -1,6 +1,7 @@
 """Parity at the five named workloads' full sizes, in the launch configuration the benchmark
-times (automatic tile height, grid and lead, interleaved order, dispatch folded into the
-Linear-1 loads), with the Expert-Wave order and the separate dispatch byte-identical to it.
+times (automatic tile height, grid, order and lead, dispatch folded into the Linear-1 loads),
+with the interleaved order, the Expert-Wave order and the separate dispatch byte-identical to
+it.
 
 Routing, the plan and the dispatched rows are checked in full. A, Yd and the output are
 compared with the oracle element by element: on every row for four workloads, and for the
@@ -116,12 +117,12 @@ def test_full_size_parity(name):
     note(f"full size {W.describe(s)}: generating")
     d = W.generate(s)
     dev = Device(d)
-    note("  gpu run (interleaved order, dispatch folded into the Linear-1 loads: the benchmark's launch)")
-    cfg = make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED)
+    note("  gpu run (automatic order, dispatch folded into the Linear-1 loads: the benchmark's launch)")
+    cfg = make_cfg(s, schedule=moe.MOE_SCHED_AUTO)
     b = run_filled(cfg, dev, gather=True)
     check_plan(cfg, b)
-    note("  gpu run (interleaved order, separate dispatch)")
-    b2 = run_filled(cfg, dev)
+    note("  gpu run (interleaved order with the D_knee lead, separate dispatch)")
+    b2 = run_filled(make_cfg(s, schedule=moe.MOE_SCHED_INTERLEAVED), dev)
     for key in ("act", "yd", "out"):
         assert torch.equal(b[key].view(torch.int16), b2[key].view(torch.int16)), key
     # dispatched rows: every row is the bit copy of its token (gathered by torch from the
