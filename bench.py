@@ -167,6 +167,9 @@ def main() -> int:
     ap.add_argument("--dispatch", choices=["fused", "separate"], default="fused",
                     help="fused: Linear-1 gathers token rows itself (moe_forward_gather); separate: "
                          "moe_dispatch writes xd first")
+    ap.add_argument("--launch", choices=["single", "calls"], default="calls",
+                    help="single: the whole layer in one kernel launch (moe_layer); calls: moe_plan, "
+                         "moe_forward_gather, moe_combine")
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--wide-tails", choices=["auto", "on", "off"], default="auto",
                     help="wide last m-blocks: the library's choice, forced on, or off (comparison)")
@@ -209,10 +212,11 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
     class Layer:
-        """One workload's inputs on the GPU, with the buffers of one schedule."""
+        """One workload's inputs on the GPU, with the buffers of one schedule (and launch)."""
 
-        def __init__(self, s, inputs, name):
-            self.s, self.name = s, name
+        def __init__(self, s, inputs, name, single=False):
+            self.s, self.single = s, single
+            self.name = name + ("_single" if single else "")
             self.x, self.logits, self.w1, self.w2 = inputs
             self.cfg = moe.MoeConfig(T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, experts_per_wave=s.experts_per_wave,
                                      schedule=sched[name], lead_waves=0 if name == "auto" else args.lead,
@@ -231,6 +235,16 @@ def main() -> int:
             def mark(i):
                 if ev is not None:
                     ev[i].record(stream)
+
+            if self.single:  # one launch: the forward events bracket the whole layer
+                mark(0)
+                if five:
+                    mark(1)
+                mark(2 if five else 1)
+                moe.moe_layer(c, self.logits, b, self.x, self.w1, self.w2, b["act"], b["yd"], b["out"], b["ws"])
+                mark(3 if five else 2)
+                mark(4 if five else 3)
+                return
 
             mark(0)
             moe.moe_plan(c, self.logits, b, b["ws"])
@@ -296,7 +310,7 @@ def main() -> int:
     # ---- the headline workload
     s, data, inputs = load_inputs(args.workload)
     flops = 6.0 * s.T * s.k * s.H * s.I
-    main_l = Layer(s, inputs, args.schedule)
+    main_l = Layer(s, inputs, args.schedule, single=args.launch == "single")
     for _ in range(args.warmup):
         main_l.step()
     main_l.check()
@@ -325,7 +339,9 @@ def main() -> int:
     order_used = main_l.order_used()
     schedules = None
     if not args.no_compare and args.trials > 0:
-        others_l = [Layer(s, inputs, n) for n in ("auto", "interleaved", "expert_wave") if n != args.schedule]
+        others_l = [Layer(s, inputs, n) for n in ("auto", "interleaved", "expert_wave") if n != main_l.name]
+        if args.schedule == "auto":  # the same order in the other launch form
+            others_l.append(Layer(s, inputs, "auto", single=args.launch != "single"))
         for l in others_l:
             for _ in range(args.warmup):
                 l.step()
@@ -371,12 +387,13 @@ def main() -> int:
     fwd_ms = float(np.mean(fwd_ms_all))
     traffic = traffic_from_profiles(args.workload)
     mfma, achieved, gbps = gemm_roofline(s, counts, fwd_ms)
+    kname = "gemm_persistent_kernel" + (" (single launch: the whole layer)" if args.launch == "single" else "")
     if mfma:
-        roof = {"bound": "mfma", "kernel": "gemm_persistent_kernel", "achieved": round(achieved, 3),
+        roof = {"bound": "mfma", "kernel": kname, "achieved": round(achieved, 3),
                 "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic}
     else:
-        roof = {"bound": "hbm", "kernel": "gemm_persistent_kernel", "achieved": round(gbps, 1),
+        roof = {"bound": "hbm", "kernel": kname, "achieved": round(gbps, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "tflops": round(achieved, 3)}
     rec = {
@@ -393,7 +410,8 @@ def main() -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
-                   "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "dispatch": args.dispatch,
+                   "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "launch": args.launch,
+                   "dispatch": args.dispatch,
                    "lead_waves": args.lead, "wide_tails": args.wide_tails, "order_used": order_used,
                    "lead_used": lead_used,
                    "tile_m": layout["tile_m"], "seed": s.seed},
@@ -426,13 +444,15 @@ def main() -> int:
         so, _, inp = load_inputs(name)
         names = [args.schedule] if args.no_compare else \
             [args.schedule] + [n for n in ("auto", "interleaved", "expert_wave") if n != args.schedule]
-        ls = [Layer(so, inp, n) for n in names]
+        ls = [Layer(so, inp, n, single=args.launch == "single" and i == 0) for i, n in enumerate(names)]
+        if not args.no_compare and args.schedule == "auto":
+            ls.append(Layer(so, inp, "auto", single=args.launch != "single"))
         for l in ls:
             for _ in range(args.warmup):
                 l.step()
         res = alternate(ls, max(args.trials, 1))
         c = ls[0].b["counts"].cpu().numpy()
-        lay, fw = res[args.schedule]
+        lay, fw = res[ls[0].name]
         fmean = float(np.mean(fw))
         mfma_o, ach, gb = gemm_roofline(so, c, fmean)
         fl = 6.0 * so.T * so.k * so.H * so.I

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* Status codes. */
 typedef enum {
@@ -218,6 +218,8 @@ typedef struct moe_ws_layout {
   size_t wave_table;    /* int32[24 + 10 (E + 1)] at most: per expert wave its tile counts,
                            unit prefix sums and list positions, and each expert's first
                            m-block and first row, from which moe_plan places the tiles */
+  size_t layer_sync;    /* 4 KiB: moe_layer's phase-barrier counters, one per 128-byte line
+                           (zero before the first moe_layer on a workspace; left zero) */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;
@@ -296,6 +298,30 @@ moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, cons
  *   yd [T*k, H] bf16 in; out [T, H] bf16 out. */
 moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint16_t* yd,
                        uint16_t* out, void* stream);
+
+/* The whole layer in ONE kernel launch (X-Stage paper, Introduction, MegaMoE paragraph: one
+ * persistent kernel runs every stage of the layer). The persistent grid first routes the token
+ * chunks, then its last workgroup to arrive writes the schedule while the others wait, then
+ * all scatter the chunks and place the tile list; after a grid-wide barrier they run the tiles
+ * (Linear-1 gathering token rows from x through perm, SwiGLU, Linear-2), and after another
+ * one the combine. Same kernels' arithmetic as moe_plan + moe_forward_gather + moe_combine:
+ * rt, act, yd and out are byte-identical to them.
+ *   logits, rt, x, w1, w2, act, yd, out, ws: as for those calls.
+ * The workspace's phase counters (moe_ws_layout.layer_sync) must be zero before its first
+ * moe_layer (a zero-filled workspace); every launch leaves them zero. The grid's workgroups wait for one another, so
+ * they must all be resident at once: the grid is sized to the resident capacity, and a kernel
+ * running concurrently on another stream can keep some from starting; every wait is bounded
+ * (spin_limit), and an expired one records MOE_ERR_TIMEOUT (moe_status_read) with the outputs
+ * undefined, and never hangs or faults. After moe_layer the workspace holds its plan, ready
+ * for moe_forward / moe_forward_gather as after moe_plan. It always runs regular tiles (no
+ * wide last m-blocks, whatever the flags say; the bytes are the same), so a later
+ * moe_forward on that plan must be given MOE_FLAG_NO_WIDE_TAILS.
+ * Errors: as moe_plan; MOE_ERR_INVALID_ARG for a non-NULL cfg->trace (trace the separate
+ * calls); MOE_ERR_UNSUPPORTED with more than 64 expert waves when they also exceed the
+ * workgroup's threads (512 for 256-row tiles, else 256). */
+moe_status moe_layer(const moe_config* cfg, const float* logits, const moe_routing* rt, const uint16_t* x,
+                     const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd, uint16_t* out, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* ---- Layer without caller-provided workspace ----
  * For callers that cannot allocate device memory: code under HIP graph capture, tight serving

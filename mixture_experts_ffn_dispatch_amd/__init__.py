@@ -11,7 +11,7 @@ from ._lib import (  # noqa: F401
     MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
     MOE_FLAG_FORCE_WAIT_TIMEOUT, MOE_FLAG_NO_WIDE_TAILS, MOE_FLAG_WIDE_TAILS, MOE_OK, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, MOE_SCHED_AUTO, LIB_PATH,
     MoeConfig, MoeError, abi_version, load, moe_burst_clock_hz, moe_burst_gap, moe_combine, moe_dispatch, moe_forward,
-    moe_forward_gather, moe_layer_noalloc, moe_plan, MOE_STATIC_WORKSPACE_BYTES,
+    moe_forward_gather, moe_layer, moe_layer_noalloc, moe_plan, MOE_STATIC_WORKSPACE_BYTES,
     moe_status_read, moe_workspace_layout, moe_workspace_size, strerror,
 )
 
@@ -48,9 +48,13 @@ def alloc_buffers(cfg: MoeConfig, device="cuda", xd=True) -> dict:
     return b
 
 
-def run_layer(cfg: MoeConfig, bufs: dict, x, logits, w1, w2, stream=None, gather=False) -> None:
+def run_layer(cfg: MoeConfig, bufs: dict, x, logits, w1, w2, stream=None, gather=False, fused=False) -> None:
     """plan -> dispatch -> forward -> combine on one stream (asynchronous); with ``gather``,
-    plan -> forward_gather (dispatch folded into the Linear-1 loads) -> combine."""
+    plan -> forward_gather (dispatch folded into the Linear-1 loads) -> combine; with
+    ``fused``, the single launch of moe_layer."""
+    if fused:
+        moe_layer(cfg, logits, bufs, x, w1, w2, bufs["act"], bufs["yd"], bufs["out"], bufs["ws"], stream)
+        return
     moe_plan(cfg, logits, bufs, bufs["ws"], stream)
     if gather:
         moe_forward_gather(cfg, bufs, x, w1, w2, bufs["act"], bufs["yd"], bufs["ws"], stream)

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
-ABI_VERSION = 5  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
+ABI_VERSION = 6  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -50,7 +50,7 @@ class CRouting(ctypes.Structure):
 class CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
-        "tasks", "unit_start", "group_units", "group_tasks", "wave_table")] + [(n, ctypes.c_int32) for n in (
+        "tasks", "unit_start", "group_units", "group_tasks", "wave_table", "layer_sync")] + [(n, ctypes.c_int32) for n in (
             "chunks", "chunk_tokens", "max_mblk", "max_tasks", "max_slots", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
             "n2_tiles")]
 
@@ -132,6 +132,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
                                                 vp]),
         "moe_combine": (ctypes.c_int32, [P(CConfig), P(CRouting), vp, vp, vp]),
         "moe_status_read": (ctypes.c_int32, [vp, ctypes.c_size_t, vp]),
+        "moe_layer": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "moe_layer_noalloc": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, vp, vp, vp, vp, vp, vp, vp]),
         "moe_burst_gap": (ctypes.c_int32, [P(CBurstCfg), vp, ctypes.c_size_t, vp, vp]),
         "moe_burst_clock_hz": (ctypes.c_int32, [P(ctypes.c_int64)]),
@@ -231,6 +232,13 @@ def moe_forward_gather(cfg, rt: dict, x, w1, w2, act, yd, ws, stream=None) -> No
 def moe_combine(cfg, rt: dict, yd, out, stream=None) -> None:
     _check(load().moe_combine(ctypes.byref(_cfg(cfg)), ctypes.byref(_routing(rt)), _ptr(yd), _ptr(out),
                               _stream(stream)), "moe_combine")
+
+
+def moe_layer(cfg, logits, rt: dict, x, w1, w2, act, yd, out, ws, stream=None) -> None:
+    """The whole layer in one kernel launch (ws must be zero-filled before its first use)."""
+    _check(load().moe_layer(ctypes.byref(_cfg(cfg)), _ptr(logits), ctypes.byref(_routing(rt)), _ptr(x), _ptr(w1),
+                            _ptr(w2), _ptr(act), _ptr(yd), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                            _stream(stream)), "moe_layer")
 
 
 def moe_layer_noalloc(cfg, logits, rt: dict, x, w1, w2, act, yd, out, status=None, stream=None) -> None:

@@ -112,6 +112,8 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   off = align_up(off + (size_t)max_slots * 16, 256);
   L->wave_table = off;
   off = align_up(off + ((size_t)kWaveTableHead + 10 * ((size_t)c->E + 1)) * 4, 256);
+  L->layer_sync = off;
+  off = align_up(off + (size_t)kLayerSyncBytes, 256);
   L->total_bytes = off;
   return MOE_OK;
 }
@@ -183,16 +185,9 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
 }
 
 namespace {
-moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
-                     size_t ws_bytes, void* stream) {
-  moe_ws_layout L;
-  moe_status st = compute_layout(cfg, &L);
-  if (st != MOE_OK) return st;
-  if (!logits || !rt || !ws || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm ||
-      !rt->pos)
-    return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
-  PlanArgs a;
+// The planner's arguments for cfg (validated) and a workspace laid out as L.
+void fill_plan_args(const moe_config* cfg, const moe_ws_layout& L, const float* logits, const moe_routing* rt,
+                    void* ws, PlanArgs& a) {
   a.logits = logits;
   a.topk_ids = rt->topk_ids;
   a.topk_w = rt->topk_w;
@@ -230,6 +225,19 @@ moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routi
   a.xs_issue_s = (cfg->xs_issue_us > 0.f ? (double)cfg->xs_issue_us : kLocalIssueUs) * 1e-6;
   a.xs_drain_bps = (cfg->xs_drain_gbps > 0.f ? (double)cfg->xs_drain_gbps : kLocalDrainGBps) * 1e9;
   a.xs_capacity_b = (cfg->xs_capacity_mib > 0.f ? (double)cfg->xs_capacity_mib : kLocalCapacityMiB) * 1048576.0;
+}
+
+moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if (!logits || !rt || !ws || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm ||
+      !rt->pos)
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  PlanArgs a;
+  fill_plan_args(cfg, L, logits, rt, ws, a);
   if (gemm_grid(L.tile_m, a.wide_tails != 0, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;
@@ -255,16 +263,11 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
 }
 
 namespace {
-// shared by moe_forward (rows from xd) and moe_forward_gather (rows from x through perm)
-moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_t* x, const int32_t* perm,
-                        const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws,
-                        size_t ws_bytes, void* stream) {
-  moe_ws_layout L;
-  moe_status st = compute_layout(cfg, &L);
-  if (st != MOE_OK) return st;
-  if ((!xd && !(x && perm)) || !w1 || !w2 || !act || !yd || !ws) return MOE_ERR_INVALID_ARG;
-  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
-  GemmArgs g;
+// The persistent GEMM's arguments for cfg (validated) and a workspace laid out as L: rows from
+// xd, or (xd NULL) from x through perm.
+void fill_gemm_args(const moe_config* cfg, const moe_ws_layout& L, const uint16_t* xd, const uint16_t* x,
+                    const int32_t* perm, const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd,
+                    void* ws, GemmArgs& g) {
   g.xd = xd;
   g.x = x;
   g.perm = perm;
@@ -294,6 +297,21 @@ moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
   g.trace = static_cast<moe_trace_rec*>(cfg->trace);
+}
+}  // namespace
+
+namespace {
+// shared by moe_forward (rows from xd) and moe_forward_gather (rows from x through perm)
+moe_status forward_impl(const moe_config* cfg, const uint16_t* xd, const uint16_t* x, const int32_t* perm,
+                        const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd, void* ws,
+                        size_t ws_bytes, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if ((!xd && !(x && perm)) || !w1 || !w2 || !act || !yd || !ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  GemmArgs g;
+  fill_gemm_args(cfg, L, xd, x, perm, w1, w2, act, yd, ws, g);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (launch_gemm(g, L.tile_m, plan_wide_tails(cfg, L.tile_m), cfg->num_workgroups, s) != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
@@ -311,6 +329,38 @@ moe_status moe_forward_gather(const moe_config* cfg, const moe_routing* rt, cons
                               void* stream) {
   if (!rt || !rt->perm || !x) return MOE_ERR_INVALID_ARG;
   return forward_impl(cfg, nullptr, x, rt->perm, w1, w2, act, yd, ws, ws_bytes, stream);
+}
+
+moe_status moe_layer(const moe_config* cfg, const float* logits, const moe_routing* rt, const uint16_t* x,
+                     const uint16_t* w1, const uint16_t* w2, uint16_t* act, uint16_t* yd, uint16_t* out, void* ws,
+                     size_t ws_bytes, void* stream) {
+  moe_ws_layout L;
+  moe_status st = compute_layout(cfg, &L);
+  if (st != MOE_OK) return st;
+  if (!logits || !rt || !rt->topk_ids || !rt->topk_w || !rt->counts || !rt->offsets || !rt->perm || !rt->pos ||
+      !x || !w1 || !w2 || !act || !yd || !out || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (cfg->trace) return MOE_ERR_INVALID_ARG;  // the traced instances are the separate forward calls'
+  if (ws_bytes < L.total_bytes) return MOE_ERR_WORKSPACE;
+  LayerArgs la;
+  fill_plan_args(cfg, L, logits, rt, ws, la.pl);
+  la.pl.wide_tails = 0;  // the single launch runs regular tiles (the same bytes as wide ones)
+  const bool wide = false;
+  if (gemm_grid(L.tile_m, wide, cfg->num_workgroups, &la.pl.grid) != hipSuccess) return MOE_ERR_HIP;
+  // the schedule step runs on one workgroup of the GEMM's size: with more than 64 expert
+  // waves it takes one thread per wave
+  const int nw = (cfg->E + la.pl.W - 1) / la.pl.W;
+  const int nt = L.tile_m == 256 ? 512 : 256;
+  if (nw > 64 && nw > nt) return MOE_ERR_UNSUPPORTED;
+  fill_gemm_args(cfg, L, nullptr, x, rt->perm, w1, w2, act, yd, ws, la.g);
+  la.topk_w = rt->topk_w;
+  la.pos = rt->pos;
+  la.out = out;
+  la.segs = combine_segments(cfg->T, cfg->H);
+  la.sync = at<int32_t>(ws, L.layer_sync);
+  if (launch_layer(la, L.tile_m, wide, cfg->num_workgroups, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 namespace {

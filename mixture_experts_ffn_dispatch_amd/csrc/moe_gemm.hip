@@ -32,7 +32,9 @@
 //  * With a trace buffer, every tile's claim, wait, main loop, epilogue and release are
 //    timed with the real-time counter (Section 5 of the paper instruments its kernel per tile
 //    the same way); without one, none of it runs.
+#include "moe_combine_dev.h"
 #include "moe_internal.h"
+#include "moe_plan_dev.h"
 
 namespace moe {
 namespace {
@@ -66,12 +68,6 @@ __device__ inline int hw_id() {
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kRsrcWord3);
-}
-
-__device__ inline unsigned pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even (v_cvt_pk_bf16_f32)
-  return (unsigned)__builtin_bit_cast(unsigned short, a) |
-         ((unsigned)__builtin_bit_cast(unsigned short, b) << 16);
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at lds_dst + 16 L
@@ -111,8 +107,176 @@ struct Interleave {
   }
 };
 
-template <int BM, int WN, int WM, int MINW, bool WIDE, bool TRACE>
-__global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(GemmArgs p) {
+// LDS bytes of a tile shape's two stages (weight rows then token rows, 64 K-columns each).
+template <int BM, int WN, int WM, bool WIDE>
+struct GemmLds {
+  static constexpr bool WIDE_OK = WIDE && BM == 256 && WN == 2 && WM == 4;
+  static constexpr int BYTES = 2 * (WIDE_OK ? 2 * kTileN2 + BM / 2 : kTileN2 + BM) * kTileK * 2;
+};
+
+// ---- the single-launch layer: phase barriers across the persistent grid ----
+// Every workgroup of the grid is resident at once (the grid never exceeds the resident
+// capacity), so a workgroup can wait for all others. Barrier n (1, 2, 3 in a launch) is
+// hierarchical, like the locality groups: a workgroup drains its stores, releases at agent
+// scope and counts itself on its group's line; the group's last arrival counts the group on
+// the all-groups line; the last group's arrival opens barrier n by writing n into every
+// group's go word (after barrier 1, only once the schedule is written). A wait polls its own
+// group's go word (bounded by spin_limit) and acquires. The counters only grow during a
+// launch (barrier n is complete at n arrivals per member), and the last workgroup to exit
+// sets them back to zero. bc: two LDS words for the broadcast to the workgroup.
+
+__device__ inline int* sync_line(int32_t* sync, int line) { return sync + line * kSyncLine; }
+
+// Counts this workgroup on `lines` (group arrivals at line lines + g, groups at line `all`)
+// for the n-th time; true (on every thread) when it was the last arrival of the whole grid,
+// which then holds (acquired) every other arrival's release.
+__device__ bool layer_count(int32_t* sync, int lines, int all, int n, int* bc) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int G = (int)gridDim.x, ng = min(G, kGroups), g = (int)blockIdx.x % kGroups;
+    const int members = (G - g + kGroups - 1) / kGroups;
+    int last = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int c = __hip_atomic_fetch_add(sync_line(sync, lines + g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c + 1 == n * members) {  // the group's last: count the group
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      const int d = __hip_atomic_fetch_add(sync_line(sync, all), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d + 1 == n * ng) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        last = 1;
+      }
+    }
+    bc[0] = last;
+  }
+  __syncthreads();
+  return bc[0] != 0;
+}
+
+// Opens barrier n for every group (called by the grid's last arrival, one thread enough).
+__device__ void layer_open(int32_t* sync, int n) {
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int ng = min((int)gridDim.x, kGroups);
+    for (int h = 0; h < ng; ++h)
+      __hip_atomic_store(sync_line(sync, kSyncGo + h), n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waits until barrier n is open for this workgroup's group; false (on every thread) when the
+// bounded wait expired.
+__device__ bool layer_wait(int32_t* sync, int n, int spin_limit, int* bc) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int* go = sync_line(sync, kSyncGo + (int)blockIdx.x % kGroups);
+    int ok = 1, spins = 0;
+    // a poll about every microsecond: up to 64 workgroups share a go word, and the grid's
+    // polls should not crowd the memory path of the workgroup that writes the schedule
+    while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
+      if (++spins > spin_limit) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(32);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    bc[1] = ok;
+  }
+  __syncthreads();
+  return bc[1] != 0;
+}
+
+// A full barrier n: arrive, the grid's last arrival opens it, wait.
+__device__ bool layer_barrier(int32_t* sync, int n, int spin_limit, int* bc) {
+  if (layer_count(sync, kSyncArrive, kSyncAll, n, bc)) layer_open(sync, n);
+  return layer_wait(sync, n, spin_limit, bc);
+}
+
+// The planner's phases of the single-launch layer, on every workgroup of the grid: route the
+// token chunks (grid-stride); the last workgroup to arrive scans the counts and writes the
+// schedule while the others wait for it; scatter the chunks and place the tile list; then
+// all wait until every workgroup is done. lds: the kernel's LDS array (lds_elems bf16); the
+// planner uses its first 54 KiB, the barrier broadcasts its last 16 bytes. Returns false when
+// a wait expired: the workgroup then runs no later phase, which would read an unfinished plan.
+template <int NT>
+__device__ bool layer_plan_phases(const LayerArgs& f, uint16_t* lds, int lds_elems) {
+  const PlanArgs& a = f.pl;
+  int* const il = reinterpret_cast<int*>(lds);
+  int* const bc = reinterpret_cast<int*>(lds + lds_elems) - 4;
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  for (int c = b; c < a.chunks; c += G) route_chunk<NT>(a, c, il);
+  if (layer_count(f.sync, kSyncArrive, kSyncAll, 1, bc)) {
+    // every chunk's counts are in: this workgroup writes the schedule, then opens barrier 1
+    int* const s_tmp = il;
+    int* const s_cnt = il + 32;
+    int* const s_tab = s_cnt + MOE_MAX_EXPERTS;
+    double* const s_cost = reinterpret_cast<double*>(s_tab + ((kWaveTableLds + 1) & ~1));
+    scan_schedule_block<NT>(a, s_tmp, s_cnt, s_tab, s_cost);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    layer_open(f.sync, 1);
+  }
+  if (!layer_wait(f.sync, 1, f.g.spin_limit, bc)) return false;
+  for (int c = b; c < a.chunks; c += G) scatter_chunk<NT>(a, c, il);
+  place_tiles<NT>(a, b, min(G, kPlaceBlocks), il);
+  return layer_barrier(f.sync, 2, f.g.spin_limit, bc);
+}
+
+// Resets the plan's cursors and ready counters (one workgroup of NT threads), so the next
+// moe_forward on this plan starts clean without a separate launch.
+template <int NT>
+__device__ void reset_tile_state(const GemmArgs& p) {
+  const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
+  for (int i = threadIdx.x; i < n; i += NT) p.mb_ready[i] = 0;
+  if (threadIdx.x == 0) {
+    p.hdr[HDR_CURSOR] = 0;
+    for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;
+    p.hdr[HDR_DONE] = 0;
+  }
+}
+
+// After the tile loop of the single-launch layer: wait until every workgroup has finished its
+// tiles, combine (grid-stride over tokens and column segments, one wavefront per item), then
+// the last workgroup out resets the barriers and the tile state for the next launch and
+// reports an expired wait in the error word.
+template <int NT>
+__device__ void layer_finish_phases(const LayerArgs& f, uint16_t* lds, int lds_elems, bool ok) {
+  int* const bc = reinterpret_cast<int*>(lds + lds_elems) - 4;
+  const int G = (int)gridDim.x;
+  if (ok) ok = layer_barrier(f.sync, 3, f.g.spin_limit, bc);
+  if (ok) {
+    constexpr int NW = NT / 64;
+    combine_items<8>(f.pos, f.topk_w, f.g.yd, f.out, f.g.T, f.g.H, f.g.k, f.g.R, f.segs,
+                     (int)blockIdx.x * NW + (int)(threadIdx.x >> 6), G * NW);
+  } else if (threadIdx.x == 0) {
+    atomicCAS(sync_line(f.sync, kSyncErr), 0, (int)MOE_ERR_TIMEOUT);
+  }
+  if (layer_count(f.sync, kSyncExit, kSyncAllExit, 1, bc)) {
+    reset_tile_state<NT>(f.g);
+    if (threadIdx.x < kLayerSyncBytes / 4 / kSyncLine) {  // one thread per line
+      int* const line = sync_line(f.sync, threadIdx.x);
+      if (threadIdx.x == kSyncErr && line[0]) atomicCAS(f.g.hdr + HDR_ERROR, 0, line[0]);
+      line[0] = 0;
+    }
+  }
+}
+
+template <bool FUSED>
+struct KernelArgsOf {
+  using T = GemmArgs;
+};
+template <>
+struct KernelArgsOf<true> {
+  using T = LayerArgs;
+};
+__device__ __forceinline__ const GemmArgs& gemm_args_of(const GemmArgs& a) { return a; }
+__device__ __forceinline__ const GemmArgs& gemm_args_of(const LayerArgs& a) { return a.g; }
+
+// FUSED: the single-launch layer (the planner's phases, then the tiles, then the combine);
+// otherwise the persistent GEMM alone.
+template <int BM, int WN, int WM, int MINW, bool WIDE, bool TRACE, bool FUSED>
+__global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typename KernelArgsOf<FUSED>::T ka) {
+  const GemmArgs& p = gemm_args_of(ka);
   constexpr int BN = kTileN2;  // weight rows per tile (Linear-1: 128 gate + 128 up)
   constexpr int BK = kTileK;
   constexpr int FN = BN / WN / 32;  // 32x32 MFMA blocks per wave along weight rows
@@ -142,6 +306,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
   // per-tile trace: only the TRACE instances (launched when a trace buffer is given) hold
   // any of its code, so the others are unchanged by it
   constexpr bool tracing = TRACE;
+  // the single-launch layer plans first; the tile loop reads the header the plan writes
+  bool plan_ok = true;
+  if constexpr (FUSED) plan_ok = layer_plan_phases<64 * WN * WM>(ka, lds, 2 * STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, LDS chunk slot
@@ -192,6 +359,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     npend = 0;
   };
   for (;;) {
+    if constexpr (FUSED) {
+      if (!plan_ok) break;  // a barrier expired: the plan may be unfinished
+    }
     long long t_claim = 0;
     if constexpr (tracing) t_claim = rt_clock();
     if (tid == 0) {
@@ -533,28 +703,33 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(Gem
     __syncthreads();
   }
 
-  // the last workgroup to leave resets the cursor and the ready counters, so the next
-  // moe_forward on this plan starts clean without a separate launch
-  if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(&p.hdr[HDR_DONE], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = done == (int)gridDim.x - 1;
-  }
-  __syncthreads();
-  if (*s_last) {
-    const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
-    for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
+  if constexpr (FUSED) {
+    layer_finish_phases<NT>(ka, lds, 2 * STAGE, plan_ok);
+  } else {
+    // the last workgroup to leave resets the cursor and the ready counters, so the next
+    // moe_forward on this plan starts clean without a separate launch
     if (tid == 0) {
-      p.hdr[HDR_CURSOR] = 0;
-      for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;
-      p.hdr[HDR_DONE] = 0;
+      const int done = __hip_atomic_fetch_add(&p.hdr[HDR_DONE], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      *s_last = done == (int)gridDim.x - 1;
+    }
+    __syncthreads();
+    if (*s_last) {
+      const int n = min(p.hdr[HDR_NMBLK], p.max_mblk);
+      for (int i = tid; i < n; i += NT) p.mb_ready[i] = 0;
+      if (tid == 0) {
+        p.hdr[HDR_CURSOR] = 0;
+        for (int g = 0; g < kGroups; ++g) p.hdr[HDR_GROUP_CURSOR + g] = 0;
+        p.hdr[HDR_DONE] = 0;
+      }
     }
   }
 }
 
 template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t variant_grid(int num_workgroups, int* grid) {
-  // the traced instance has the same resources' limits: the grid is sized on the plain one
-  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false>;
+  // the traced and single-launch instances have the same resource limits (launch bounds and
+  // LDS): the grid is sized on the plain one
+  auto kern = gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false, false>;
   // resident capacity: the grid never exceeds it, so every workgroup runs at once and each
   // group has workgroups that can take its sublist's tiles
   int dev = 0, cus = 0, per_cu = 0;
@@ -572,8 +747,8 @@ hipError_t variant_grid(int num_workgroups, int* grid) {
 
 template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) {
-  auto kern = a.trace ? gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, true>
-                      : gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false>;
+  auto kern = a.trace ? gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, true, false>
+                      : gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false, false>;
   constexpr int NT = 64 * WN * WM;
   int grid = 0;
   hipError_t err = variant_grid<BM, WN, WM, MINW, WIDE>(num_workgroups, &grid);
@@ -584,7 +759,39 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
   return hipGetLastError();
 }
 
+template <int BM, int WN, int WM, int MINW, bool WIDE>
+hipError_t launch_layer_variant(const LayerArgs& a, int num_workgroups, hipStream_t s) {
+  constexpr int NT = 64 * WN * WM;
+  // the planner's phases share the tile loop's LDS: the scan needs about 54 KiB
+  static_assert(GemmLds<BM, WN, WM, WIDE>::BYTES >= 32 * 4 + 4 * MOE_MAX_EXPERTS + 4 * (kWaveTableLds + 1) +
+                                                      8 * MOE_MAX_EXPERTS + 16,
+                "LDS for the planner phases");
+  static_assert(GemmLds<BM, WN, WM, WIDE>::BYTES >= 4 * (NT / 64) * MOE_MAX_EXPERTS + 16 &&
+                GemmLds<BM, WN, WM, WIDE>::BYTES >= 4 * kWaveTableLds + 16, "LDS for the scatter");
+  int grid = 0;
+  hipError_t err = variant_grid<BM, WN, WM, MINW, WIDE>(num_workgroups, &grid);
+  if (err != hipSuccess) return err;
+  if (grid != a.pl.grid) return hipErrorInvalidValue;  // the plan's lead rule assumed this grid
+  LayerArgs la = a;
+  la.g.ngroups = grid >= kGroups ? kGroups : 1;
+  hipLaunchKernelGGL((gemm_persistent_kernel<BM, WN, WM, MINW, WIDE, false, true>), dim3(grid), dim3(NT), 0, s, la);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_layer(const LayerArgs& a, int tile_m, bool wide, int num_workgroups, hipStream_t s) {
+  // the single launch runs regular tiles only: in the wide instance the planner's code pushes
+  // the tile loop's scalar registers into scratch memory (moe_layer plans without wide tiles)
+  if (wide) return hipErrorInvalidValue;
+  switch (tile_m) {
+    case 256: return launch_layer_variant<256, 2, 4, 2, false>(a, num_workgroups, s);
+    case 128: return launch_layer_variant<128, 2, 2, 1, false>(a, num_workgroups, s);
+    case 64: return launch_layer_variant<64, 4, 1, 2, false>(a, num_workgroups, s);
+    case 32: return launch_layer_variant<32, 4, 1, 2, false>(a, num_workgroups, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, bool wide, int num_workgroups, hipStream_t s) {
   switch (tile_m) {

@@ -144,6 +144,26 @@ struct GemmArgs {
   moe_trace_rec* trace;  // per-tile records (moe_config.trace), or null
 };
 
+// The single-launch layer kernel: plan, the persistent GEMM with the dispatch gather, combine.
+struct LayerArgs {
+  GemmArgs g;      // gather mode: Linear-1 reads token rows of x through perm
+  PlanArgs pl;     // the planner's arguments (pl.grid = the launch's grid)
+  const float* topk_w;
+  const int32_t* pos;
+  uint16_t* out;
+  int segs;        // column segments per token row in the combine
+  int32_t* sync;   // the phase barriers' counters (kLayerSyncBytes, zero between launches)
+};
+
+// The single-launch layer's phase barriers: one 128-byte line (32 ints) per counter, so that
+// the groups' counters sit on separate cache lines. Lines 0-7: each locality group's
+// arrivals; 8: the groups whose every workgroup has arrived; 9-16: each group's "go" word
+// (the last barrier the group may pass); 17: a timeout to report; 18-25: each group's exits;
+// 26: the groups whose every workgroup has exited.
+constexpr int kLayerSyncBytes = 4096;
+constexpr int kSyncLine = 32;  // ints per line
+constexpr int kSyncArrive = 0, kSyncAll = 8, kSyncGo = 9, kSyncErr = 17, kSyncExit = 18, kSyncAllExit = 26;
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s);
 hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s);
@@ -156,6 +176,8 @@ hipError_t launch_combine(const int32_t* pos, const float* w, const uint16_t* yd
 hipError_t launch_gemm(const GemmArgs& a, int tile_m, bool wide, int num_workgroups, hipStream_t s);
 // The grid launch_gemm uses for this tile height and request (every workgroup resident at once).
 hipError_t gemm_grid(int tile_m, bool wide, int num_workgroups, int* grid);
+// The single-launch layer kernel on the grid gemm_grid gives (la.pl.grid must hold it).
+hipError_t launch_layer(const LayerArgs& la, int tile_m, bool wide, int num_workgroups, hipStream_t s);
 
 // Whether moe_plan writes wide last m-blocks, and moe_forward launches the kernel instance that
 // runs them: only with 256-row tiles; MOE_FLAG_WIDE_TAILS / MOE_FLAG_NO_WIDE_TAILS force the
@@ -166,6 +188,16 @@ inline bool plan_wide_tails(const moe_config* c, int tile_m) {
   if (c->flags & MOE_FLAG_WIDE_TAILS) return true;
   return (long long)c->T * c->k <= 3ll * 256 * c->E;
 }
+// Column segments per token row: with few tokens, rows are cut into up to 4 segments of at
+// least 128 chunks (one step of a wavefront) so that about 4096 wavefronts run.
+inline int combine_segments(int T, int H) {
+  const int cpr = H / 8;
+  int segs = (4096 + T - 1) / T;
+  segs = segs < 1 ? 1 : segs > 4 ? 4 : segs;
+  while (segs > 1 && cpr / segs < 128) --segs;
+  return segs;
+}
+
 // Burst-Gap microbenchmark: `producers` workgroups, each storing `bytes` per burst into its own
 // `region` of buf, `periods` times, with a busy gap of `gap_ticks` real-time counter ticks.
 hipError_t launch_burst_gap(uint8_t* buf, size_t region, int producers, int bytes, int periods,

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.abi_version() == 5
+    assert moe.abi_version() == 6
 
 
 
