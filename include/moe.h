@@ -269,6 +269,14 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
 
 /* Expert FFN over all dispatched rows in one persistent launch (its last workgroup resets the
  * plan's counters, so moe_forward may be repeated on one plan).
+ * Progress: the grid is sized so that all of its workgroups are resident at once, and each of
+ * the 8 locality groups (workgroup index mod 8, one XCD each) walks its own part of the tile
+ * list first and takes the other groups' parts once its own is used up. A Linear-2 tile waits
+ * for Linear-1 tiles that may sit in another group's part, so every group needs resident
+ * workgroups for the launch to make progress: a kernel running concurrently on another
+ * stream that keeps a whole XCD busy can stall those waits until the bounded wait expires
+ * (MOE_ERR_TIMEOUT, outputs undefined; no hang). Run it with the GPU to itself, or with
+ * num_workgroups below the free capacity of every XCD. */
  *   xd  [T*k, H] bf16 dispatched rows (from moe_dispatch)
  *   w1  [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up (out x in, like nn.Linear.weight)
  *   w2  [E, H, I] bf16

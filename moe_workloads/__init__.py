@@ -22,7 +22,8 @@ from dataclasses import dataclass, replace
 
 import numpy as np
 
-__all__ = ["MoeShape", "SHAPES", "SHAPE_ORDER", "shape", "generate", "flops", "nthreads"]
+__all__ = ["MoeShape", "SHAPES", "SHAPE_ORDER", "shape", "generate", "flops", "nthreads",
+           "AttnShape", "ATTN_SHAPES", "attn_shape", "generate_attention"]
 
 _BLOCK = 1 << 22  # elements per independently seeded block
 
@@ -172,3 +173,53 @@ def describe(s: MoeShape) -> str:
 def gflop(s: MoeShape) -> float:
     return flops(s) / 1e9
 
+
+
+# ---------------------------------------------------------------- attention inputs
+# The paper's second workload (Section 4.3): full, non-causal attention of a DiT after the
+# Ulysses all-to-all, one GPU holding every token of its share of the heads, head dimension
+# 128. Q, K and V are float32 N(0, 1) draws rounded to bfloat16 (stored [B, heads, M, d]).
+
+_T_Q, _T_K, _T_V = 10, 11, 12
+
+
+@dataclass(frozen=True)
+class AttnShape:
+    """Shape and seed of one synthetic attention workload."""
+
+    name: str
+    B: int
+    heads: int  # heads on this GPU
+    M: int      # sequence length (every token of the sequence)
+    d: int      # head dimension
+    seed: int
+
+    @property
+    def flops(self) -> int:
+        return 4 * self.B * self.heads * self.M * self.M * self.d
+
+
+ATTN_SHAPES = {
+    # a ragged sequence the oracle finishes at once
+    "attn_tiny": AttnShape("attn_tiny", 1, 2, 300, 128, 2001),
+    # one GPU's share of a 40-head, d = 128 video DiT under 8-way Ulysses: 5 heads, 32K tokens
+    "attn_dit_share": AttnShape("attn_dit_share", 1, 5, 32768, 128, 2002),
+}
+
+
+def attn_shape(name: str | None = None, **kw) -> AttnShape:
+    if name is not None:
+        s = ATTN_SHAPES[name]
+        return replace(s, **kw) if kw else s
+    kw.setdefault("name", "custom_attn")
+    kw.setdefault("seed", 9)
+    return AttnShape(**kw)
+
+
+def generate_attention(s: AttnShape, threads: int | None = None) -> dict:
+    """q, k, v: uint16 [B, heads, M, d] bfloat16 bits of N(0, 1) draws."""
+    n = s.B * s.heads * s.M * s.d
+    shape4 = (s.B, s.heads, s.M, s.d)
+    with _cf.ThreadPoolExecutor(threads or nthreads()) as pool:
+        return {name: _draw_normal_bf16(s.seed, t, n, 1.0, pool).reshape(shape4)
+                for name, t in (("q", _T_Q), ("k", _T_K), ("v", _T_V))}

@@ -17,6 +17,8 @@ Modules:
   moe_ref     the plain definition, float64 with explicit bfloat16 rounding points
   brute       scalar pure-Python loops (exact rationals where possible) for micro shapes
   invariants  special-case builders (identical experts, one expert, exact-integer case)
+  burst_gap   the Burst-Gap model of Section 3 (issue time, period, capacity, design test)
+  attention_ref  the attention forward of Section 4.3 (full, non-causal softmax(QK^T/sqrt(d))V)
 
 Pins: every function here is checked by ``tests/test_oracle_*.py`` against something other
 than itself (hand-worked golden cases, closed forms, library routines, brute force,
