@@ -128,6 +128,54 @@ def cpu_baseline(s, data, budget_s: float = 10.0) -> dict:
                       f"routing of all {s.T} tokens charged pro rata; {t_total:.1f} s"}
 
 
+def attention_block(name, steps, warmup, moe, W, log) -> dict:
+    """The attention forward of the X-Stage paper's Section 4.3 on one workload: event-timed
+    launches, TFLOP/s against the bf16 MFMA peak, and the paper's design test for its output
+    bursts (each persistent workgroup stores one b_m x d bf16 tile at a tile boundary, the next
+    tile's Q-loop is the gap) against this GPU's own memory path."""
+    import numpy as np
+    import torch
+
+    s = W.attn_shape(name)
+    log(f"attention {s.name}: B={s.B} heads={s.heads} M={s.M} d={s.d}")
+    g = W.generate_attention(s)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v = dev(g["q"]), dev(g["k"]), dev(g["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty((s.B, s.heads, s.M), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        moe.attn_forward(s.B, s.heads, s.M, q, k, v, o, lse)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        moe.attn_forward(s.B, s.heads, s.M, q, k, v, o, lse)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    t = float(np.median(ms)) * 1e-3
+    tflops = s.flops / t / 1e12
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    bm = moe._lib.ATTN_TILE_QUERIES
+    tiles = s.B * s.heads * -(-s.M // bm)
+    grid = min(cus * moe._lib.ATTN_WORKGROUPS_PER_CU, tiles)
+    rounds = -(-tiles // grid)
+    qloop = t / rounds  # one tile's Q-loop: the gap between a workgroup's output bursts
+    burst = bm * s.d * 2  # bytes per workgroup per tile boundary
+    v_agg = grid * burst   # aligned producers, the conservative case
+    r, t0, cap = 6646e9, 0.927e-6, 31.2 * 2 ** 20  # this GPU's own memory (moe_burst_gap)
+    return {"workload": s.name, "B": s.B, "heads": s.heads, "M": s.M, "d": s.d, "kernel": "attn_fwd_kernel",
+            "us": stats_us(ms), "tflops": round(tflops, 2), "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS, 4),
+            "tiles": tiles, "grid": grid, "qloop_us": round(qloop * 1e6, 2),
+            "burst_bytes_per_tile": burst, "aligned_burst_bytes": v_agg,
+            "design_test_local": {"rate_bound": v_agg / r <= t0 + qloop, "capacity_bound": v_agg - r * t0 <= cap,
+                                  "recovery_gap_us": round((v_agg / r - t0) * 1e6, 3)}}
+
+
 def host_cpu() -> dict:
     model = "unknown"
     try:
@@ -183,6 +231,8 @@ def main() -> int:
     ap.add_argument("--lib", default=None, help="load another build of libmoe (same ABI) instead of the in-tree one")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--attention", default="attn_dit_share",
+                    help="also time the attention forward on this workload ('none': skip)")
     ap.add_argument("--trace-summary", default=None,
                     help="also run one traced layer per schedule of the headline workload and write "
                          "its per-tile phases to this file")
@@ -469,6 +519,8 @@ def main() -> int:
         rec["workloads"][name] = w
         del ls, inp
         torch.cuda.empty_cache()
+    if args.attention != "none":
+        rec["attention"] = attention_block(args.attention, args.steps, args.warmup, moe, W, log)
     if cpu is not None:
         rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)

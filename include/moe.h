@@ -276,7 +276,7 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
  * workgroups for the launch to make progress: a kernel running concurrently on another
  * stream that keeps a whole XCD busy can stall those waits until the bounded wait expires
  * (MOE_ERR_TIMEOUT, outputs undefined; no hang). Run it with the GPU to itself, or with
- * num_workgroups below the free capacity of every XCD. */
+ * num_workgroups below the free capacity of every XCD.
  *   xd  [T*k, H] bf16 dispatched rows (from moe_dispatch)
  *   w1  [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up (out x in, like nn.Linear.weight)
  *   w2  [E, H, I] bf16

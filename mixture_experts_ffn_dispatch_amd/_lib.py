@@ -28,6 +28,8 @@ MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
 MOE_FLAG_NO_WIDE_TAILS = 0x2
 MOE_FLAG_WIDE_TAILS = 0x4
 MOE_STATIC_WORKSPACE_BYTES = 8 << 20  # workspace array of moe_layer_noalloc
+ATTN_TILE_QUERIES = 128  # include/attn.h
+ATTN_WORKGROUPS_PER_CU = 2
 
 
 class MoeError(RuntimeError):
@@ -64,6 +66,11 @@ class CTraceRec(ctypes.Structure):
 TRACE_DTYPE = [("task", "<i4"), ("workgroup", "<i4"), ("xcc", "<i4"), ("hw_id", "<i4"), ("t_claim", "<i8"),
                ("t_claimed", "<i8"), ("t_start", "<i8"), ("t_epilogue", "<i8"), ("t_end", "<i8"),
                ("t_release", "<i8")]
+
+
+class CAttnConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("B", "heads", "M", "d", "num_workgroups")] + [
+        ("reserved", ctypes.c_int32 * 3)]
 
 
 class CBurstCfg(ctypes.Structure):
@@ -135,6 +142,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "moe_layer": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "moe_layer_noalloc": (ctypes.c_int32, [P(CConfig), vp, P(CRouting), vp, vp, vp, vp, vp, vp, vp, vp]),
         "moe_burst_gap": (ctypes.c_int32, [P(CBurstCfg), vp, ctypes.c_size_t, vp, vp]),
+        "attn_forward": (ctypes.c_int32, [P(CAttnConfig), vp, vp, vp, vp, vp, vp]),
         "moe_burst_clock_hz": (ctypes.c_int32, [P(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
@@ -248,6 +256,14 @@ def moe_layer_noalloc(cfg, logits, rt: dict, x, w1, w2, act, yd, out, status=Non
     _check(load().moe_layer_noalloc(ctypes.byref(_cfg(cfg)), _ptr(logits), ctypes.byref(_routing(rt)), _ptr(x),
                                     _ptr(w1), _ptr(w2), _ptr(act), _ptr(yd), _ptr(out), _ptr(status),
                                     _stream(stream)), "moe_layer_noalloc")
+
+
+def attn_forward(B: int, heads: int, M: int, q, k, v, o, lse=None, d: int = 128, num_workgroups: int = 0,
+                 stream=None) -> None:
+    """Attention forward (include/attn.h): q, k, v, o [B, heads, M, d] bf16; lse float32 or None."""
+    c = CAttnConfig(B=B, heads=heads, M=M, d=d, num_workgroups=num_workgroups)
+    _check(load().attn_forward(ctypes.byref(c), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(stream)),
+           "attn_forward")
 
 
 def moe_burst_gap(producers: int, nbytes: int, periods: int, gap_ticks: int, buf, times, stream=None) -> None:

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.hip", "moe_plan.hip", "moe_combine.hip", "moe_gemm.hip", "moe_xstage.hip"]
+SOURCES = ["moe_api.hip", "moe_plan.hip", "moe_combine.hip", "moe_gemm.hip", "moe_xstage.hip", "attn_fwd.hip"]
 ARCH = "gfx950"
 
 

@@ -11,12 +11,29 @@ from mixture_experts_ffn_dispatch_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
+ATTN_HEADER = os.path.join(ROOT, "include", "attn.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in (HEADER, ATTN_HEADER):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b((?:moe|attn)_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_headers_compile_as_c_and_cpp(tmp_path):
+    # both headers are plain C: the host compilers accept them on their own
+    import shutil
+    import subprocess
+
+    src = tmp_path / "h.c"
+    src.write_text('#include "moe.h"\n#include "attn.h"\nint main(void) { return (int)sizeof(moe_config); }\n')
+    for cc, extra in (("gcc", ["-std=c99"]), ("g++", ["-x", "c++", "-std=c++17"])):
+        if shutil.which(cc):
+            r = subprocess.run([cc, *extra, "-fsyntax-only", "-Wall", "-Werror", f"-I{os.path.dirname(HEADER)}", str(src)],
+                               capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr
 
 
 def test_library_exports_every_declared_symbol():
@@ -35,8 +52,9 @@ def test_binding_matches_header():
     assert int(re.search(r"#define MOE_ABI_VERSION (\d+)", text).group(1)) == _lib.ABI_VERSION
     for struct, cls in (("moe_config", _lib.CConfig), ("moe_routing", _lib.CRouting),
                         ("moe_ws_layout", _lib.CLayout), ("moe_burst_cfg", _lib.CBurstCfg),
-                        ("moe_trace_rec", _lib.CTraceRec)):
-        body = re.search(r"typedef struct " + struct + r" \{(.*?)\} " + struct + ";", text, flags=re.S).group(1)
+                        ("moe_trace_rec", _lib.CTraceRec), ("attn_config", _lib.CAttnConfig)):
+        src = text if struct != "attn_config" else re.sub(r"/\*.*?\*/", "", open(ATTN_HEADER).read(), flags=re.S)
+        body = re.search(r"typedef struct " + struct + r" \{(.*?)\} " + struct + ";", src, flags=re.S).group(1)
         assert re.findall(r"(\w+)(?:\[\d+\])?;", body) == [n for n, _ in cls._fields_], struct
 
 
@@ -165,3 +183,24 @@ def test_undersized_workspace_rejected():
         moe.MOE_ERR_WORKSPACE
     assert lib.moe_forward_gather(ctypes.byref(c), ctypes.byref(rt), dummy, dummy, dummy, dummy, dummy, dummy,
                                   need - 1, None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_attention_rejects_invalid_configs_on_the_host():
+    lib = moe.load()
+    dummy = 1 << 20
+
+    def call(**kw):
+        base = dict(B=1, heads=1, M=64, d=128, num_workgroups=0)
+        base.update(kw)
+        c = _lib.CAttnConfig(**base)
+        return lib.attn_forward(ctypes.byref(c), dummy, dummy, dummy, dummy, None, None)
+
+    assert call(M=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(B=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(heads=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(d=64) == moe.MOE_ERR_UNSUPPORTED
+    assert call(M=1 << 23) == moe.MOE_ERR_UNSUPPORTED  # a head of 2 GiB
+    c = _lib.CAttnConfig(B=1, heads=1, M=64, d=128)
+    assert lib.attn_forward(ctypes.byref(c), None, dummy, dummy, dummy, None, None) == moe.MOE_ERR_INVALID_ARG
+    c.reserved[1] = 1
+    assert lib.attn_forward(ctypes.byref(c), dummy, dummy, dummy, dummy, None, None) == moe.MOE_ERR_INVALID_ARG
