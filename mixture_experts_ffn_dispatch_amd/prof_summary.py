@@ -14,7 +14,7 @@ import csv
 import json
 import sys
 
-KERNELS = ("gemm_persistent_kernel", "route_hist_kernel", "scan_schedule_kernel", "scatter_kernel",
+KERNELS = ("gemm_persistent_kernel", "attn_fwd_kernel", "route_hist_kernel", "scan_schedule_kernel", "scatter_kernel",
            "dispatch_kernel", "combine_kernel", "copyBuffer")
 
 
