@@ -305,49 +305,76 @@ __device__ inline void step_sync() {
   }
 }
 
-// Predicted cost (seconds) of one candidate order of the MOE_SCHED_AUTO rule (include/moe.h):
-// D = 0 is the Expert-Wave order, D >= 1 the interleaved order with lead D. Needs the tile
-// counts (t.a, t.b), their prefix sums (t.p1, t.p2, totals A and B), the expert offsets (t.off)
-// and whether the GEMM is HBM-bound. The same double-precision steps as the rule's statement,
-// without fused multiply-adds, so a host model can reproduce the choice exactly.
-__device__ double auto_cost(const PlanArgs& a, const WaveTable& t, int nw, int D, long long A, long long B,
-                            bool hbm_bound) {
+// The MOE_SCHED_AUTO rule (include/moe.h) prices each candidate order: D = 0 is the
+// Expert-Wave order, D >= 1 the interleaved order with lead D. Its model of the GEMM's tile
+// main loops and bursts, and the dependency-distance test (as for lead 0 above).
+struct AutoModel {
+  double t1, t2, vt, R, T0, Q;
+  long long den, need;
+  __device__ AutoModel(const PlanArgs& a, long long A, long long B) {
 #pragma clang fp contract(off)
-  const double G = (double)a.grid, BM = (double)a.tile_m;
-  const double t1 = G * fmax(2.0 * BM * 256.0 * (double)a.H / kAutoMfmaFlops, 512.0 * (double)a.H / kAutoStreamBytes);
-  const double t2 = G * fmax(2.0 * BM * 256.0 * (double)a.I / kAutoMfmaFlops, 512.0 * (double)a.I / kAutoStreamBytes);
-  const double vt = BM * 256.0 * 2.0;
-  const double R = a.xs_drain_bps, T0 = a.xs_issue_s, Q = a.xs_capacity_b;
-  const long long den = A * a.H + B * a.I;
-  const long long need = (long long)a.grid * a.H * (A + B);
+    const double G = (double)a.grid, BM = (double)a.tile_m;
+    t1 = G * fmax(2.0 * BM * 256.0 * (double)a.H / kAutoMfmaFlops, 512.0 * (double)a.H / kAutoStreamBytes);
+    t2 = G * fmax(2.0 * BM * 256.0 * (double)a.I / kAutoMfmaFlops, 512.0 * (double)a.I / kAutoStreamBytes);
+    vt = BM * 256.0 * 2.0;
+    R = a.xs_drain_bps;
+    T0 = a.xs_issue_s;
+    Q = a.xs_capacity_b;
+    den = A * a.H + B * a.I;
+    need = (long long)a.grid * a.H * (A + B);
+  }
+};
+
+// Wave i's share of candidate D's price: the X-Stage stall of its Linear-2 bursts (>= 0),
+// returned with the sign bit set when its Linear-2 tiles can be reached before its Linear-1
+// tiles are done (a dependency stall of half a Linear-1 tile); +0 for a wave with no
+// Linear-2 tiles. The same double-precision steps as the rule's statement, without fused
+// multiply-adds, so a host model can reproduce the choice exactly.
+__device__ double auto_term(const PlanArgs& a, const WaveTable& t, const AutoModel& m, int nw, int D, int i) {
+#pragma clang fp contract(off)
+  const int b = t.b[i];
+  if (b == 0) return 0.0;
+  // the producers whose Linear-2 boundaries align: those on Linear-2 tiles at a time, the
+  // Linear-2 share of the segment's work when Linear-1 tiles of wave i + D are spread in it
+  const int an = (D > 0 && i + D < nw) ? t.a[i + D] : 0;
+  const double share = ((double)b * m.t2) / ((double)b * m.t2 + (double)an * m.t1);
+  const double kact = fmax(1.0, (double)min(a.grid, b) * share);
+  const double V = kact * m.vt;
+  const double g = m.t2;
+  double T = fmax(m.T0, V / m.R - g);
+  if (V - m.R * m.T0 > m.Q) T = fmax(T, (V - m.Q) / m.R);
+  const double xs = ((double)b / kact) * (T - m.T0);
+  bool reach = true;
+  if (D > 0) {
+    const long long dist =
+        (long long)t.p2[i] - t.p2[max(0, i - D + 1)] + t.p1[min(i + D, nw)] - t.p1[min(i + 1, nw)];
+    reach = dist * m.den < m.need;
+  }
+  return reach ? -xs : xs;
+}
+
+// Candidate D's price from its waves' terms (term(i) gives wave i's auto_term), summed in
+// wave order, plus the locality cost when the GEMM is HBM-bound: the activation bytes live
+// while a wave's Linear-2 tiles run (waves i .. i + D) beyond the last-level cache.
+template <class Term>
+__device__ double auto_price(const PlanArgs& a, const WaveTable& t, const AutoModel& m, int nw, int D,
+                             bool hbm_bound, Term term) {
+#pragma clang fp contract(off)
   double xs = 0.0, dep = 0.0, over = 0.0;
   for (int i = 0; i < nw; ++i) {
-    // activation bytes live while wave i's Linear-2 tiles run: waves i .. i + D
     const int last = D > 0 ? min(i + D, nw - 1) : i;
     const double ws = (double)(t.off[min(a.E, (last + 1) * a.W)] - t.off[i * a.W]) * (double)a.I * 2.0;
     over = fmax(over, ws - kAutoCacheBytes);
-    const int b = t.b[i];
-    if (b == 0) continue;
-    // the producers whose Linear-2 boundaries align: those on Linear-2 tiles at a time, the
-    // Linear-2 share of the segment's work when Linear-1 tiles of wave i + D are spread in it
-    const int an = (D > 0 && i + D < nw) ? t.a[i + D] : 0;
-    const double share = ((double)b * t2) / ((double)b * t2 + (double)an * t1);
-    const double kact = fmax(1.0, (double)min(a.grid, b) * share);
-    const double V = kact * vt;
-    const double g = t2;
-    double T = fmax(T0, V / R - g);
-    if (V - R * T0 > Q) T = fmax(T, (V - Q) / R);
-    xs += ((double)b / kact) * (T - T0);
-    bool reach = true;
-    if (D > 0) {
-      const long long dist =
-          (long long)t.p2[i] - t.p2[max(0, i - D + 1)] + t.p1[min(i + D, nw)] - t.p1[min(i + 1, nw)];
-      reach = dist * den < need;
-    }
-    if (reach) dep += t1 / 2.0;
+    const double v = term(i);
+    xs += fabs(v);
+    if (__double_as_longlong(v) < 0) dep += m.t1 / 2.0;
   }
   return xs + dep + (hbm_bound ? over / kAutoStreamBytes : 0.0);
 }
+// Candidates of up to this many expert waves are priced with one lane per (lead, wave) term,
+// held in the (nw + 1) x nw doubles of s_cost, and one lane per lead summing them.
+constexpr int kAutoPairWaves = 31;
+static_assert((kAutoPairWaves + 1) * kAutoPairWaves <= MOE_MAX_EXPERTS, "s_cost holds the terms");
 
 // 3. tile counts per expert wave and where each wave's runs start in the list. A run (one
 //    wave's Linear-1 or Linear-2 tiles) is cut into units of kUnit consecutive tiles (the
@@ -412,17 +439,40 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
       D = step_min<ONE, NT>(cand, s_tmp);
     }
     if (automatic) {
-      // MOE_SCHED_AUTO: thread t prices the interleaved order with lead t + 1; every thread
-      // prices the Expert-Wave order and reads all prices, so all take the same choice
-      long long rows = t.off[E], active = 0;
-      for (int e = 0; e < E; ++e) active += t.off[e + 1] > t.off[e] ? 1 : 0;
+      // MOE_SCHED_AUTO: every candidate is priced and all threads read all prices, so all
+      // take the same choice
+      constexpr int kStride = ONE ? 64 : NT;
+      int act = 0;
+      for (int e = tid; e < E; e += kStride) act += t.off[e + 1] > t.off[e] ? 1 : 0;
+      int active;
+      (void)step_scan<ONE, NT>(act, s_tmp, active);
+      const long long rows = t.off[E];
       const double flops = 6.0 * (double)rows * (double)a.H * (double)a.I;
       const double bytes = (double)rows * (double)a.H * 4.0 + (double)active * 6.0 * (double)a.H * (double)a.I +
                            (double)rows * (double)a.I * 4.0;
       const bool hbm_bound = bytes / kAutoStreamBytes > flops / kAutoMfmaFlops;
-      if (tid < nw) s_cost[tid] = auto_cost(a, t, nw, tid + 1, A, B, hbm_bound);
-      const double ew = auto_cost(a, t, nw, 0, A, B, hbm_bound);
-      step_sync<ONE>();
+      const AutoModel m(a, A, B);
+      double ew;
+      if (ONE && nw <= kAutoPairWaves) {
+        // s_cost[D * nw + i] = wave i's term of candidate D (D = 0 .. nw); then lane D sums its
+        // row and the prices go to s_cost[D - 1] (lead D) and s_cost[nw] (Expert-Wave)
+        for (int p = tid; p < (nw + 1) * nw; p += kStride) s_cost[p] = auto_term(a, t, m, nw, p / nw, p % nw);
+        step_sync<ONE>();
+        double price = 0.0;
+        if (tid <= nw)
+          price = auto_price(a, t, m, nw, tid, hbm_bound, [&](int i) { return s_cost[tid * nw + i]; });
+        step_sync<ONE>();
+        if (tid <= nw) s_cost[tid == 0 ? nw : tid - 1] = price;
+        step_sync<ONE>();
+        ew = s_cost[nw];
+      } else {
+        // thread t prices the interleaved order with lead t + 1, every thread the Expert-Wave one
+        if (tid < nw)
+          s_cost[tid] = auto_price(a, t, m, nw, tid + 1, hbm_bound,
+                                   [&](int i) { return auto_term(a, t, m, nw, tid + 1, i); });
+        ew = auto_price(a, t, m, nw, 0, hbm_bound, [&](int i) { return auto_term(a, t, m, nw, 0, i); });
+        step_sync<ONE>();
+      }
       double best = s_cost[0];
       int bestD = 1;
       for (int d = 1; d < nw; ++d)
@@ -506,7 +556,7 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
 
 // The schedule step on one NT-thread workgroup. LDS: s_tmp[32], s_cnt[MOE_MAX_EXPERTS] (rows
 // routed to each expert), s_tab[kWaveTableLds] (the wave table), s_cost[MOE_MAX_EXPERTS]
-// (MOE_SCHED_AUTO: price of each interleave lead). With more than 64 expert waves it needs
+// (MOE_SCHED_AUTO: the prices of the candidate orders and their per-wave terms). With more than 64 expert waves it needs
 // nw <= NT (the host checks).
 template <int NT>
 __device__ void scan_schedule_block(const PlanArgs& a, int* s_tmp, int* s_cnt, int* s_tab, double* s_cost) {

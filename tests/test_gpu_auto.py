@@ -58,3 +58,28 @@ def test_auto_outputs_equal_both_fixed_orders(cal):
     # the plan's tile list is dependency-safe for the order it chose
     hdr = plan_header(auto)
     assert int(hdr[28]) in (moe.MOE_SCHED_EXPERT_WAVE, moe.MOE_SCHED_INTERLEAVED)
+
+
+@pytest.mark.parametrize("E,W_", [(31, 1), (62, 2), (40, 1), (80, 1)])
+def test_auto_choice_at_many_waves(E, W_):
+    # 31 waves: every (lead, wave) term on a lane of its own; 40 waves: one lane per lead on
+    # wavefront 0; 80 waves: the whole workgroup. With these sizes the remote calibrations
+    # choose leads well below the number of waves, so the prices decide.
+    s = W.shape(T=75 * E, H=4096, I=2048, E=E, k=8, experts_per_wave=W_, seed=90 + E)
+    d = W.generate(s, parts=("logits",))
+    logits = torch.from_numpy(d["logits"]).cuda()
+    ids, _ = R.route(d["logits"], s.k)
+    counts = R.plan(ids, s.E)[0]
+    for cal in CALIBRATIONS:
+        cfg = make_cfg(s, schedule=moe.MOE_SCHED_AUTO, xs_issue_us=cal[0], xs_drain_gbps=cal[1],
+                       xs_capacity_mib=cal[2])
+        b = moe.alloc_buffers(cfg, xd=False)
+        moe.moe_plan(cfg, logits, b, b["ws"])
+        torch.cuda.synchronize()
+        hdr = plan_header(b)
+        L = moe.moe_workspace_layout(cfg)
+        sched, lead, _ = auto_choice(counts, W_, s.H, s.I, L["tile_m"], L["n1_tiles"], L["n2_tiles"],
+                                     int(hdr[27]), calibration(*cal))
+        note(f"E={E} W={W_} calibration {cal}: device order {hdr[28]} lead {hdr[26]}, model {sched} lead {lead}")
+        assert int(hdr[28]) == (moe.MOE_SCHED_INTERLEAVED if sched else moe.MOE_SCHED_EXPERT_WAVE)
+        assert int(hdr[26]) == lead
