@@ -218,6 +218,8 @@ def main() -> int:
     ap.add_argument("--launch", choices=["single", "calls"], default="calls",
                     help="single: the whole layer in one kernel launch (moe_layer); calls: moe_plan, "
                          "moe_forward_gather, moe_combine")
+    ap.add_argument("--plan-launches", type=int, choices=[1, 3], default=3,
+                    help="moe_plan as three launches (the default) or one launch with a grid barrier")
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--wide-tails", choices=["auto", "on", "off"], default="auto",
                     help="wide last m-blocks: the library's choice, forced on, or off (comparison)")
@@ -273,7 +275,8 @@ def main() -> int:
                                      tile_m=args.tile_m,
                                      num_workgroups=args.num_workgroups,
                                      flags={"auto": 0, "on": moe.MOE_FLAG_WIDE_TAILS,
-                                            "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails])
+                                            "off": moe.MOE_FLAG_NO_WIDE_TAILS}[args.wide_tails]
+                                     | (moe.MOE_FLAG_PLAN_ONE_LAUNCH if args.plan_launches == 1 else 0))
             self.b = moe.alloc_buffers(self.cfg, xd=not fused)
 
         def step(self, ev=None):
@@ -461,7 +464,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": s.name, "T": s.T, "H": s.H, "I": s.I, "E": s.E, "k": s.k,
                    "experts_per_wave": s.experts_per_wave, "schedule": args.schedule, "launch": args.launch,
-                   "dispatch": args.dispatch,
+                   "dispatch": args.dispatch, "plan_launches": args.plan_launches,
                    "lead_waves": args.lead, "wide_tails": args.wide_tails, "order_used": order_used,
                    "lead_used": lead_used,
                    "tile_m": layout["tile_m"], "seed": s.seed},

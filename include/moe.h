@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 /* Status codes. */
 typedef enum {
@@ -174,6 +174,12 @@ typedef struct moe_trace_rec {
 #define MOE_FLAG_NO_WIDE_TAILS 0x2
 #define MOE_FLAG_WIDE_TAILS 0x4
 
+/* moe_plan runs its steps in one launch with a grid barrier instead of three launches (route,
+   scan and schedule, scatter); the results are the same bytes. On MI355X the barrier's
+   cross-XCD atomics cost more than the two launch boundaries it replaces (the plan takes 3 to
+   15 us longer), so this is for comparison. */
+#define MOE_FLAG_PLAN_ONE_LAUNCH 0x8
+
 /* Routing buffers, written by moe_plan and read by the later calls (device pointers). */
 typedef struct moe_routing {
   int32_t* topk_ids; /* [T, k]   expert of slot (t, j); j ascending = descending router logit  */
@@ -218,8 +224,10 @@ typedef struct moe_ws_layout {
   size_t wave_table;    /* int32[24 + 10 (E + 1)] at most: per expert wave its tile counts,
                            unit prefix sums and list positions, and each expert's first
                            m-block and first row, from which moe_plan places the tiles */
-  size_t layer_sync;    /* 4 KiB: moe_layer's phase-barrier counters, one per 128-byte line
-                           (zero before the first moe_layer on a workspace; left zero) */
+  size_t layer_sync;    /* 4 KiB right after the header, at the same offset for every config:
+                           the grid-barrier counters of moe_plan and moe_layer, one per
+                           128-byte line (zero before the first call on a workspace; every
+                           launch leaves them zero) */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;
@@ -257,7 +265,15 @@ moe_status moe_workspace_layout(const moe_config* cfg, moe_ws_layout* layout);
  *     dispatched rows are expert-contiguous and, within an expert, in slot order.
  *   ws: m-block table, zeroed dependency counters, and the Linear-1/Linear-2 tile list in
  *     the order cfg->schedule asks for.
- * Three kernel launches; no host synchronisation. */
+ * Three kernel launches (route, scan and schedule, scatter and tile placement), no host
+ * synchronisation. With MOE_FLAG_PLAN_ONE_LAUNCH one launch instead: its grid of resident
+ * workgroups routes the token chunks; the last workgroup to arrive writes the schedule while
+ * the others wait at a grid barrier, then all scatter and place the tile list. Its barrier
+ * counters (moe_ws_layout.layer_sync) must then be zero before the call (a zero-filled
+ * workspace; every launch leaves them zero). That wait is bounded: if a kernel running
+ * concurrently keeps workgroups of the grid from starting until it expires, MOE_ERR_TIMEOUT
+ * is recorded (moe_status_read), the routing outputs are undefined and the tile list is left
+ * empty, so a later moe_forward runs no tile. */
 moe_status moe_plan(const moe_config* cfg, const float* logits, const moe_routing* rt, void* ws,
                     size_t ws_bytes, void* stream);
 

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
-ABI_VERSION = 6  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
+ABI_VERSION = 7  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -27,6 +27,7 @@ MOE_SCHED_AUTO = 2
 MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
 MOE_FLAG_NO_WIDE_TAILS = 0x2
 MOE_FLAG_WIDE_TAILS = 0x4
+MOE_FLAG_PLAN_ONE_LAUNCH = 0x8
 MOE_STATIC_WORKSPACE_BYTES = 8 << 20  # workspace array of moe_layer_noalloc
 ATTN_TILE_QUERIES = 128  # include/attn.h
 ATTN_WORKGROUPS_PER_CU = 2

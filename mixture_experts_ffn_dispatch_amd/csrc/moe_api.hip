@@ -40,7 +40,9 @@ moe_status check_config(const moe_config* c) {
   if (!(c->xs_issue_us >= 0.f) || !(c->xs_drain_gbps >= 0.f) || !(c->xs_capacity_mib >= 0.f) ||
       c->xs_issue_us > 1e9f || c->xs_drain_gbps > 1e9f || c->xs_capacity_mib > 1e9f)
     return MOE_ERR_INVALID_ARG;
-  if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
+  if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS |
+                   MOE_FLAG_PLAN_ONE_LAUNCH))
+    return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_NO_WIDE_TAILS) && (c->flags & MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
   if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
   if (c->tile_m != 0 && c->tile_m != 32 && c->tile_m != 64 && c->tile_m != 128 && c->tile_m != 256)
@@ -88,6 +90,11 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   size_t off = 0;
   L->header = off;
   off = align_up(off + HDR_SLOTS * 4, 256);
+  // the barrier counters of the one-launch planner and of moe_layer sit at the same offset for
+  // every config, so a workspace reused across configs (moe_layer_noalloc's array) keeps them
+  // zero between launches
+  L->layer_sync = off;
+  off = align_up(off + (size_t)kLayerSyncBytes, 256);
   L->chunk_counts = off;
   off = align_up(off + (size_t)((chunks + 3) & ~3ll) * c->E * 4, 256);
   L->mblk_expert = off;
@@ -112,8 +119,6 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   off = align_up(off + (size_t)max_slots * 16, 256);
   L->wave_table = off;
   off = align_up(off + ((size_t)kWaveTableHead + 10 * ((size_t)c->E + 1)) * 4, 256);
-  L->layer_sync = off;
-  off = align_up(off + (size_t)kLayerSyncBytes, 256);
   L->total_bytes = off;
   return MOE_OK;
 }
@@ -240,6 +245,12 @@ moe_status plan_impl(const moe_config* cfg, const float* logits, const moe_routi
   fill_plan_args(cfg, L, logits, rt, ws, a);
   if (gemm_grid(L.tile_m, a.wide_tails != 0, cfg->num_workgroups, &a.grid) != hipSuccess) return MOE_ERR_HIP;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg->flags & MOE_FLAG_PLAN_ONE_LAUNCH) {
+    // the grid barrier waits only for resident workgroups to arrive (cfg->spin_limit bounds the
+    // Linear-2 tiles' waits): the default bound
+    if (launch_plan(a, at<int32_t>(ws, L.layer_sync), kDefaultSpinLimit, s) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+  }
   if (launch_route_hist(a, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_scan_schedule(a, s) != hipSuccess) return MOE_ERR_HIP;
   if (launch_scatter(a, s) != hipSuccess) return MOE_ERR_HIP;

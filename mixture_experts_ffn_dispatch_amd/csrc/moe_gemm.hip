@@ -35,6 +35,7 @@
 #include "moe_combine_dev.h"
 #include "moe_internal.h"
 #include "moe_plan_dev.h"
+#include "moe_sync_dev.h"
 
 namespace moe {
 namespace {
@@ -114,84 +115,6 @@ struct GemmLds {
   static constexpr int BYTES = 2 * (WIDE_OK ? 2 * kTileN2 + BM / 2 : kTileN2 + BM) * kTileK * 2;
 };
 
-// ---- the single-launch layer: phase barriers across the persistent grid ----
-// Every workgroup of the grid is resident at once (the grid never exceeds the resident
-// capacity), so a workgroup can wait for all others. Barrier n (1, 2, 3 in a launch) is
-// hierarchical, like the locality groups: a workgroup drains its stores, releases at agent
-// scope and counts itself on its group's line; the group's last arrival counts the group on
-// the all-groups line; the last group's arrival opens barrier n by writing n into every
-// group's go word (after barrier 1, only once the schedule is written). A wait polls its own
-// group's go word (bounded by spin_limit) and acquires. The counters only grow during a
-// launch (barrier n is complete at n arrivals per member), and the last workgroup to exit
-// sets them back to zero. bc: two LDS words for the broadcast to the workgroup.
-
-__device__ inline int* sync_line(int32_t* sync, int line) { return sync + line * kSyncLine; }
-
-// Counts this workgroup on `lines` (group arrivals at line lines + g, groups at line `all`)
-// for the n-th time; true (on every thread) when it was the last arrival of the whole grid,
-// which then holds (acquired) every other arrival's release.
-__device__ bool layer_count(int32_t* sync, int lines, int all, int n, int* bc) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int G = (int)gridDim.x, ng = min(G, kGroups), g = (int)blockIdx.x % kGroups;
-    const int members = (G - g + kGroups - 1) / kGroups;
-    int last = 0;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int c = __hip_atomic_fetch_add(sync_line(sync, lines + g), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c + 1 == n * members) {  // the group's last: count the group
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-      const int d = __hip_atomic_fetch_add(sync_line(sync, all), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (d + 1 == n * ng) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        last = 1;
-      }
-    }
-    bc[0] = last;
-  }
-  __syncthreads();
-  return bc[0] != 0;
-}
-
-// Opens barrier n for every group (called by the grid's last arrival, one thread enough).
-__device__ void layer_open(int32_t* sync, int n) {
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int ng = min((int)gridDim.x, kGroups);
-    for (int h = 0; h < ng; ++h)
-      __hip_atomic_store(sync_line(sync, kSyncGo + h), n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Waits until barrier n is open for this workgroup's group; false (on every thread) when the
-// bounded wait expired.
-__device__ bool layer_wait(int32_t* sync, int n, int spin_limit, int* bc) {
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int* go = sync_line(sync, kSyncGo + (int)blockIdx.x % kGroups);
-    int ok = 1, spins = 0;
-    // a poll about every microsecond: up to 64 workgroups share a go word, and the grid's
-    // polls should not crowd the memory path of the workgroup that writes the schedule
-    while (__hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n) {
-      if (++spins > spin_limit) {
-        ok = 0;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(32);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    bc[1] = ok;
-  }
-  __syncthreads();
-  return bc[1] != 0;
-}
-
-// A full barrier n: arrive, the grid's last arrival opens it, wait.
-__device__ bool layer_barrier(int32_t* sync, int n, int spin_limit, int* bc) {
-  if (layer_count(sync, kSyncArrive, kSyncAll, n, bc)) layer_open(sync, n);
-  return layer_wait(sync, n, spin_limit, bc);
-}
-
 // The planner's phases of the single-launch layer, on every workgroup of the grid: route the
 // token chunks (grid-stride); the last workgroup to arrive scans the counts and writes the
 // schedule while the others wait for it; scatter the chunks and place the tile list; then
@@ -253,11 +176,7 @@ __device__ void layer_finish_phases(const LayerArgs& f, uint16_t* lds, int lds_e
   }
   if (layer_count(f.sync, kSyncExit, kSyncAllExit, 1, bc)) {
     reset_tile_state<NT>(f.g);
-    if (threadIdx.x < kLayerSyncBytes / 4 / kSyncLine) {  // one thread per line
-      int* const line = sync_line(f.sync, threadIdx.x);
-      if (threadIdx.x == kSyncErr && line[0]) atomicCAS(f.g.hdr + HDR_ERROR, 0, line[0]);
-      line[0] = 0;
-    }
+    layer_sync_reset(f.sync, f.g.hdr);
   }
 }
 

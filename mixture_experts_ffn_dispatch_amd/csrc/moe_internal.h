@@ -165,6 +165,9 @@ constexpr int kSyncLine = 32;  // ints per line
 constexpr int kSyncArrive = 0, kSyncAll = 8, kSyncGo = 9, kSyncErr = 17, kSyncExit = 18, kSyncAllExit = 26;
 
 // Launchers (return the hipError_t of the launch).
+// The planner in one launch (route, scan and schedule, scatter and tile placement); sync: the
+// workspace's barrier counters (kLayerSyncBytes, zero between launches).
+hipError_t launch_plan(const PlanArgs& a, int32_t* sync, int spin_limit, hipStream_t s);
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s);
 hipError_t launch_scan_schedule(const PlanArgs& a, hipStream_t s);
 hipError_t launch_scatter(const PlanArgs& a, hipStream_t s);

@@ -21,8 +21,14 @@
 //                  Then every block places its share of the tile list and the group records
 //                  from the wave table (each tile independently).
 //
+//   plan           all of the above in ONE launch (MOE_FLAG_PLAN_ONE_LAUNCH): a grid of resident
+//                  workgroups routes the chunks, the last one to arrive runs the scan and
+//                  schedule step while the others wait at a grid barrier, then all scatter
+//                  the chunks and place the tile list.
+//
 // The dispatch gather and the combine are in moe_combine.hip.
 #include "moe_plan_dev.h"
+#include "moe_sync_dev.h"
 
 namespace moe {
 namespace {
@@ -57,7 +63,71 @@ __global__ __launch_bounds__(kPlanThreads) void scatter_kernel(PlanArgs a) {
   place_tiles<kPlanThreads>(a, blockIdx.x, min((int)gridDim.x, kPlaceBlocks), run);
 }
 
+// The planner in one launch: the route, scan-and-schedule and scatter kernels' steps with a
+// grid barrier (moe_sync_dev.h) between routing and the schedule's readers. Every workgroup is
+// resident (the grid is capped at the resident capacity) and takes token chunks b, b + G, ...
+// The barrier counters live in the workspace (zero between launches; the last workgroup out
+// sets them back to zero); a wait that expires skips the scatter and records MOE_ERR_TIMEOUT.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a, int32_t* sync, int spin_limit) {
+  // the largest step's LDS: the scatter's 16 rows of running counts (64 KiB); the scan and
+  // schedule step needs about 54 KiB of it
+  __shared__ __align__(16) int lds[kPlanThreads / 64 * MOE_MAX_EXPERTS];
+  __shared__ int bc[2];
+  static_assert(4 * (32 + MOE_MAX_EXPERTS + ((kWaveTableLds + 1) & ~1)) + 8 * MOE_MAX_EXPERTS <= sizeof(lds),
+                "LDS of the scan and schedule step");
+  const int G = (int)gridDim.x, b = (int)blockIdx.x;
+  for (int c = b; c < a.chunks; c += G) route_chunk<kPlanThreads>(a, c, lds);
+  if (layer_count(sync, kSyncArrive, kSyncAll, 1, bc)) {
+    // every chunk's counts are in: this workgroup writes the schedule, then opens the barrier
+    int* const s_tmp = lds;
+    int* const s_cnt = lds + 32;
+    int* const s_tab = s_cnt + MOE_MAX_EXPERTS;
+    double* const s_cost = reinterpret_cast<double*>(s_tab + ((kWaveTableLds + 1) & ~1));
+    scan_schedule_block<kPlanThreads>(a, s_tmp, s_cnt, s_tab, s_cost);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    layer_open(sync, 1);
+  }
+  // short polls: at most two workgroups per CU wait, with nothing else to do
+  if (layer_wait<4>(sync, 1, spin_limit, bc)) {
+    for (int c = b; c < a.chunks; c += G) scatter_chunk<kPlanThreads>(a, c, lds);
+    place_tiles<kPlanThreads>(a, b, min(G, kPlaceBlocks), lds);
+  } else if (threadIdx.x == 0) {
+    atomicCAS(sync_line(sync, kSyncErr), 0, (int)MOE_ERR_TIMEOUT);
+  }
+  if (layer_count(sync, kSyncExit, kSyncAllExit, 1, bc)) {
+    if (sync_line(sync, kSyncErr)[0] != 0 && threadIdx.x <= kGroups) {
+      // an expired wait left perm, pos and the tile records unwritten: publish an empty tile
+      // list, so that a moe_forward on this plan runs no tile (its readers of the routing
+      // arrays skip entries out of range)
+      a.hdr[HDR_GTASK_OFF + threadIdx.x] = 0;
+      a.hdr[HDR_GROUP_OFF + threadIdx.x] = 0;
+      if (threadIdx.x == 0) {
+        a.hdr[HDR_NTASKS] = 0;
+        a.hdr[HDR_NUNITS] = 0;
+      }
+    }
+    __syncthreads();
+    layer_sync_reset(sync, a.hdr);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_plan(const PlanArgs& a, int32_t* sync, int spin_limit, hipStream_t s) {
+  // resident capacity: the grid never exceeds it, so every workgroup runs at once
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, plan_kernel, kPlanThreads, 0);
+  if (err != hipSuccess) return err;
+  const int capacity = cus * (per_cu > 0 ? per_cu : 1);
+  const int grid = a.chunks < capacity ? a.chunks : capacity;
+  hipLaunchKernelGGL(plan_kernel, dim3(grid), dim3(kPlanThreads), 0, s, a, sync, spin_limit);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_hist(const PlanArgs& a, hipStream_t s) {
   const int R = (a.E + 63) / 64;

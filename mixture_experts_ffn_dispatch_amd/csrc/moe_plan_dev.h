@@ -422,21 +422,23 @@ __device__ void schedule_waves(const PlanArgs& a, const WaveTable& t, int nw, in
         t.p2[nw] = B;
       }
       step_sync<ONE>();
-      const long long den = (long long)A * a.H + (long long)B * a.I;
-      const long long need = (long long)a.grid * a.H * (A + B);
-      int cand = nw;  // thread t tests lead t + 1
-      if (tid < nw) {
-        const int Dc = tid + 1;
-        bool ok = true;
-        for (int i = 0; i < nw && ok; ++i) {
-          if (t.b[i] == 0) continue;
-          const long long dist = (long long)t.p2[i] - t.p2[max(0, i - Dc + 1)] + t.p1[min(i + Dc, nw)] -
-                                 t.p1[min(i + 1, nw)];
-          ok = dist * den >= need;
+      if (!automatic) {
+        const long long den = (long long)A * a.H + (long long)B * a.I;
+        const long long need = (long long)a.grid * a.H * (A + B);
+        int cand = nw;  // thread t tests lead t + 1
+        if (tid < nw) {
+          const int Dc = tid + 1;
+          bool ok = true;
+          for (int i = 0; i < nw && ok; ++i) {
+            if (t.b[i] == 0) continue;
+            const long long dist = (long long)t.p2[i] - t.p2[max(0, i - Dc + 1)] + t.p1[min(i + Dc, nw)] -
+                                   t.p1[min(i + 1, nw)];
+            ok = dist * den >= need;
+          }
+          if (ok) cand = Dc;
         }
-        if (ok) cand = Dc;
+        D = step_min<ONE, NT>(cand, s_tmp);
       }
-      D = step_min<ONE, NT>(cand, s_tmp);
     }
     if (automatic) {
       // MOE_SCHED_AUTO: every candidate is priced and all threads read all prices, so all
@@ -565,6 +567,9 @@ __device__ void scan_schedule_block(const PlanArgs& a, int* s_tmp, int* s_cnt, i
   const int nw = (E + a.W - 1) / a.W;
   const WaveTable t(s_tab, nw, E);
   int* const s_off = t.off;  // expert offsets
+  // the table's unused slots (in the head, past the last wave) are written out with the rest:
+  // zero, so a plan's bytes are fixed
+  for (int i = tid; i < wave_table_len(nw, E); i += NT) s_tab[i] = 0;
   // 1. per-expert exclusive scans of the (expert, chunk) count table, in place: entry (e, c)
   //    becomes the first row of chunk c's slots among expert e's rows (the scatter adds the
   //    expert's offset), and the row total is the expert's count. Wavefront w owns rows
