@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 /* Status codes. */
 typedef enum {
@@ -180,6 +180,11 @@ typedef struct moe_trace_rec {
    15 us longer), so this is for comparison. */
 #define MOE_FLAG_PLAN_ONE_LAUNCH 0x8
 
+/* Test hook: the persistent GEMM's workgroups of locality group 0 take no tile, as if a kernel
+   running concurrently kept their XCD busy for the whole launch; the other groups must run
+   every tile (see the progress note on moe_forward). Never set in production. */
+#define MOE_FLAG_TEST_ABSENT_GROUP 0x10
+
 /* Routing buffers, written by moe_plan and read by the later calls (device pointers). */
 typedef struct moe_routing {
   int32_t* topk_ids; /* [T, k]   expert of slot (t, j); j ascending = descending router logit  */
@@ -228,6 +233,8 @@ typedef struct moe_ws_layout {
                            the grid-barrier counters of moe_plan and moe_layer, one per
                            128-byte line (zero before the first call on a workspace; every
                            launch leaves them zero) */
+  size_t defer_slots;   /* int32[2048][8]: each persistent workgroup's deferred Linear-2 tile
+                           (its record and record slot), written before it is read */
   int32_t chunks;       /* token chunks of the routing histogram                  */
   int32_t chunk_tokens; /* tokens per chunk (the last chunk may hold fewer)       */
   int32_t max_mblk;
@@ -285,14 +292,17 @@ moe_status moe_dispatch(const moe_config* cfg, const moe_routing* rt, const uint
 
 /* Expert FFN over all dispatched rows in one persistent launch (its last workgroup resets the
  * plan's counters, so moe_forward may be repeated on one plan).
- * Progress: the grid is sized so that all of its workgroups are resident at once, and each of
- * the 8 locality groups (workgroup index mod 8, one XCD each) walks its own part of the tile
- * list first and takes the other groups' parts once its own is used up. A Linear-2 tile waits
- * for Linear-1 tiles that may sit in another group's part, so every group needs resident
- * workgroups for the launch to make progress: a kernel running concurrently on another
- * stream that keeps a whole XCD busy can stall those waits until the bounded wait expires
- * (MOE_ERR_TIMEOUT, outputs undefined; no hang). Run it with the GPU to itself, or with
- * num_workgroups below the free capacity of every XCD.
+ * Progress: each of the 8 locality groups (workgroup index mod 8, one XCD each) walks its own
+ * part of the tile list first and takes the other groups' parts once its own is used up. A
+ * Linear-2 tile waits for Linear-1 tiles that may sit in another group's part; if that group
+ * has no resident workgroup (a kernel running concurrently keeps its XCD busy), a wait that
+ * lasts 1 ms sets the tile aside and its workgroup runs only tiles that cannot wait (the
+ * first unclaimed record of any group's part that is a Linear-1 tile or a ready Linear-2
+ * tile) until it is ready. So the launch finishes as long as at least one workgroup of the
+ * grid runs; what remains required is that workgroups which have started keep running. The
+ * grid is sized to the resident capacity; a wait that still exceeds spin_limit records
+ * MOE_ERR_TIMEOUT (outputs undefined; no hang). MOE_FLAG_TEST_ABSENT_GROUP forces an absent
+ * group for tests.
  *   xd  [T*k, H] bf16 dispatched rows (from moe_dispatch)
  *   w1  [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up (out x in, like nn.Linear.weight)
  *   w2  [E, H, I] bf16

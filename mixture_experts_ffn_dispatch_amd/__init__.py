@@ -9,7 +9,7 @@ from __future__ import annotations
 
 from ._lib import (  # noqa: F401
     MOE_ERR_HIP, MOE_ERR_INVALID_ARG, MOE_ERR_TIMEOUT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE,
-    MOE_FLAG_FORCE_WAIT_TIMEOUT, MOE_FLAG_NO_WIDE_TAILS, MOE_FLAG_WIDE_TAILS, MOE_FLAG_PLAN_ONE_LAUNCH, MOE_OK, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, MOE_SCHED_AUTO, LIB_PATH,
+    MOE_FLAG_FORCE_WAIT_TIMEOUT, MOE_FLAG_NO_WIDE_TAILS, MOE_FLAG_WIDE_TAILS, MOE_FLAG_PLAN_ONE_LAUNCH, MOE_FLAG_TEST_ABSENT_GROUP, MOE_OK, MOE_SCHED_EXPERT_WAVE, MOE_SCHED_INTERLEAVED, MOE_SCHED_AUTO, LIB_PATH,
     MoeConfig, MoeError, abi_version, attn_forward, load, moe_burst_clock_hz, moe_burst_gap, moe_combine, moe_dispatch, moe_forward,
     moe_forward_gather, moe_layer, moe_layer_noalloc, moe_plan, MOE_STATIC_WORKSPACE_BYTES,
     moe_status_read, moe_workspace_layout, moe_workspace_size, strerror,

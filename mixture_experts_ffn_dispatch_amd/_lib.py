@@ -12,7 +12,7 @@ from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
-ABI_VERSION = 7  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
+ABI_VERSION = 8  # MOE_ABI_VERSION of include/moe.h that this binding marshals for
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = -1
@@ -28,6 +28,7 @@ MOE_FLAG_FORCE_WAIT_TIMEOUT = 0x1
 MOE_FLAG_NO_WIDE_TAILS = 0x2
 MOE_FLAG_WIDE_TAILS = 0x4
 MOE_FLAG_PLAN_ONE_LAUNCH = 0x8
+MOE_FLAG_TEST_ABSENT_GROUP = 0x10
 MOE_STATIC_WORKSPACE_BYTES = 8 << 20  # workspace array of moe_layer_noalloc
 ATTN_TILE_QUERIES = 128  # include/attn.h
 ATTN_WORKGROUPS_PER_CU = 2
@@ -53,7 +54,7 @@ class CRouting(ctypes.Structure):
 class CLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "total_bytes", "header", "chunk_counts", "mblk_expert", "mblk_row0", "mblk_rows", "mblk_ready",
-        "tasks", "unit_start", "group_units", "group_tasks", "wave_table", "layer_sync")] + [(n, ctypes.c_int32) for n in (
+        "tasks", "unit_start", "group_units", "group_tasks", "wave_table", "layer_sync", "defer_slots")] + [(n, ctypes.c_int32) for n in (
             "chunks", "chunk_tokens", "max_mblk", "max_tasks", "max_slots", "tile_m", "tile_n1", "tile_n2", "n1_tiles",
             "n2_tiles")]
 

@@ -41,7 +41,7 @@ moe_status check_config(const moe_config* c) {
       c->xs_issue_us > 1e9f || c->xs_drain_gbps > 1e9f || c->xs_capacity_mib > 1e9f)
     return MOE_ERR_INVALID_ARG;
   if (c->flags & ~(MOE_FLAG_FORCE_WAIT_TIMEOUT | MOE_FLAG_NO_WIDE_TAILS | MOE_FLAG_WIDE_TAILS |
-                   MOE_FLAG_PLAN_ONE_LAUNCH))
+                   MOE_FLAG_PLAN_ONE_LAUNCH | MOE_FLAG_TEST_ABSENT_GROUP))
     return MOE_ERR_INVALID_ARG;
   if ((c->flags & MOE_FLAG_NO_WIDE_TAILS) && (c->flags & MOE_FLAG_WIDE_TAILS)) return MOE_ERR_INVALID_ARG;
   if (c->reserved != 0) return MOE_ERR_INVALID_ARG;
@@ -117,6 +117,8 @@ moe_status compute_layout(const moe_config* c, moe_ws_layout* L) {
   L->max_slots = (int32_t)max_slots;
   L->group_tasks = off;
   off = align_up(off + (size_t)max_slots * 16, 256);
+  L->defer_slots = off;
+  off = align_up(off + (size_t)kDeferSlots * 32, 256);
   L->wave_table = off;
   off = align_up(off + ((size_t)kWaveTableHead + 10 * ((size_t)c->E + 1)) * 4, 256);
   L->total_bytes = off;
@@ -307,6 +309,8 @@ void fill_gemm_args(const moe_config* cfg, const moe_ws_layout& L, const uint16_
   g.max_mblk = L.max_mblk;
   g.spin_limit = cfg->spin_limit > 0 ? cfg->spin_limit : kDefaultSpinLimit;
   g.force_timeout = (cfg->flags & MOE_FLAG_FORCE_WAIT_TIMEOUT) ? 1 : 0;
+  g.absent_group = (cfg->flags & MOE_FLAG_TEST_ABSENT_GROUP) ? 0 : -1;
+  g.defer = at<int32_t>(ws, L.defer_slots);
   g.trace = static_cast<moe_trace_rec*>(cfg->trace);
 }
 }  // namespace

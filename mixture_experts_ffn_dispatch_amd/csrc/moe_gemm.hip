@@ -218,8 +218,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
   static_assert(!WIDE_OK || (LD == LDN + BM / RG + 2 && (BM / 2) % RG == 0), "wide staging");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
-  // The tile record, its trace slot and the exit flag live at the start of LDS stage 1: that
-  // stage is first written only after a barrier that every wave passes after reading them.
+  // The tile record, its record slot, the resume and defer flags and the exit flag live at the
+  // start of LDS stage 1: that stage is first written only after a barrier that every wave
+  // passes after reading them.
   int* const s_task = reinterpret_cast<int*>(&lds[STAGE]);
   int* const s_last = s_task + 5;
   // per-tile trace: only the TRACE instances (launched when a trace buffer is given) hold
@@ -255,6 +256,19 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
   // Linear-2 tiles that wait for it lie a whole wave later in the list: an interleaved order
   // with a lead of at least two waves. Otherwise every completion is released at once.
   const int batch = p.hdr[HDR_LEAD] >= 2 ? kReleaseBatch : 1;
+  // Progress without every group resident. A Linear-2 tile can wait for Linear-1 tiles in
+  // another group's list, which only that group's workgroups take until their own lists run
+  // out. If a group has no resident workgroup (a kernel running concurrently keeps its XCD
+  // busy), such a wait would last until the bounded wait expires. So a Linear-2 tile whose
+  // m-block is not ready after kDeferTicks (far longer than any wait with every group
+  // resident) is set aside in the workgroup's deferral slot, and the workgroup then runs only
+  // tiles that cannot wait: the first unclaimed record of any group's list if it is a
+  // Linear-1 tile or a ready Linear-2 tile (a compare-and-swap on that group's cursor),
+  // releasing each Linear-1 completion at once, until the deferred tile is ready. The
+  // earliest unfinished tile of the whole list is then always running, or deferred and ready,
+  // or first in its group's list and runnable, so a single resident workgroup finishes the
+  // list. Only the group lists need it (a shared cursor hands out the list in order).
+  bool have_def = false;             // a deferred Linear-2 tile waits in this workgroup's slot
   int npend = 0;                     // completions held (the same value in every lane)
   int pend_mb[kReleaseBatch] = {};  // thread 0: their m-blocks
   int pend_slot[kReleaseBatch] = {};  // thread 0: their trace records
@@ -277,16 +291,74 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     }
     npend = 0;
   };
+  // MOE_FLAG_TEST_ABSENT_GROUP: this group's workgroups take no tile
+  const bool absent = p.ngroups > 1 && my_group == p.absent_group;
   for (;;) {
     if constexpr (FUSED) {
       if (!plan_ok) break;  // a barrier expired: the plan may be unfinished
     }
+    if (absent) break;
     long long t_claim = 0;
     if constexpr (tracing) t_claim = rt_clock();
     if (tid == 0) {
       i32x4 rec = {kNoTask, -1, 0, 0};  // task word, expert, first row, rows
       int slot = -1;                    // its trace record: the list position or record slot
-      if (p.ngroups == 1) {
+      int resumed = 0;                  // 1: the deferred tile, ready; 2: its wait expired
+      if (have_def) {
+        int* const def = p.defer + 8 * blockIdx.x;
+        const i32x4 d = {__hip_atomic_load(def, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(def + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(def + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                         __hip_atomic_load(def + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+        const int dslot = __hip_atomic_load(def + 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // whether a Linear-2 record's m-block has all its Linear-1 releases
+        auto ready = [&](const i32x4& r) {
+          const int m = (r[0] >> kTaskMblkShift) & ((1 << kTaskMblkBits) - 1);
+          if (m >= p.max_mblk) return true;  // malformed: the tile's own checks reject it
+          const int need = ((WIDE_OK && (r[3] & kRowsWide)) ? (p.n1 + 1) / 2 : p.n1) + p.force_timeout;
+          return __hip_atomic_load(&p.mb_ready[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= need;
+        };
+        for (int spins = 0;; ++spins) {
+          if (ready(d)) {
+            rec = d;
+            slot = dslot;
+            resumed = 1;
+            break;
+          }
+          bool got = false;
+          for (int h = 0; h < p.ngroups && !got; ++h) {
+            const int g = (my_group + h) % p.ngroups;
+            int* const cur = &p.hdr[HDR_GROUP_CURSOR + g];
+            const int lo = max(p.hdr[HDR_GTASK_OFF + g], 0), hi = min(p.hdr[HDR_GTASK_OFF + g + 1], p.max_slots);
+            int c = __hip_atomic_load(cur, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            while (c >= 0 && c < hi - lo) {
+              const i32x4 r = *reinterpret_cast<const i32x4*>(p.gtasks + 4 * (size_t)(lo + c));
+              if (r[0] != kNopTask && ((unsigned)r[0] >> kTaskL2Bit) != 0u && !ready(r)) break;
+              if (__hip_atomic_compare_exchange_strong(cur, &c, c + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)) {
+                if (r[0] == kNopTask) {  // a spare slot: the next record
+                  ++c;
+                  continue;
+                }
+                rec = r;
+                slot = lo + c;
+                got = true;
+                break;
+              }
+              // the cursor moved: c holds its new value
+            }
+          }
+          if (got) break;
+          if (spins >= p.spin_limit) {  // run it anyway, as an expired wait does
+            atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_TIMEOUT);
+            rec = d;
+            slot = dslot;
+            resumed = 2;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(8);
+        }
+      } else if (p.ngroups == 1) {
         const int ntasks = min(p.hdr[HDR_NTASKS], p.max_tasks);
         for (;;) {
           const int t = atomicAdd(&p.hdr[HDR_CURSOR], 1);
@@ -326,7 +398,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
       s_task[1] = rec[1];
       s_task[2] = rec[2];
       s_task[3] = rec[3];
-      if constexpr (tracing) s_task[4] = slot;
+      s_task[4] = slot;
+      s_task[6] = resumed;
     }
     __syncthreads();
     long long t_claimed = 0;
@@ -345,7 +418,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     const int e = __builtin_amdgcn_readfirstlane(s_task[1]);
     const int row0 = __builtin_amdgcn_readfirstlane(s_task[2]);
     const int rows_word = __builtin_amdgcn_readfirstlane(s_task[3]);
-    const int slot = tracing ? __builtin_amdgcn_readfirstlane(s_task[4]) : -1;
+    const int slot = __builtin_amdgcn_readfirstlane(s_task[4]);
+    const int resumed = __builtin_amdgcn_readfirstlane(s_task[6]);
+    if (resumed) have_def = false;
     const bool wide = WIDE_OK && (rows_word & kRowsWide) != 0;
     const int nrows = rows_word & ~kRowsWide;
     // a plan this workspace could not have produced: skip the tile, report, never fault
@@ -368,17 +443,32 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
       if (tid == 0) {
         // every Linear-1 tile of the m-block releases once; a wide m-block has half as many
         const int need = (wide ? (p.n1 + 1) / 2 : p.n1) + p.force_timeout;
-        int spins = 0;
+        // a tile may be set aside once (not a resumed one, and one at a time)
+        const bool may_defer = p.ngroups > 1 && !have_def && resumed == 0 && blockIdx.x < (unsigned)kDeferSlots;
+        const long long t_wait = may_defer ? rt_clock() : 0;
+        int spins = 0, defer_now = 0;
         while (__hip_atomic_load(&p.mb_ready[mb], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
           if (++spins > p.spin_limit) {
             atomicCAS(&p.hdr[HDR_ERROR], 0, (int)MOE_ERR_TIMEOUT);
             break;
           }
+          if (may_defer && rt_clock() - t_wait > kDeferTicks) {
+            int* const def = p.defer + 8 * blockIdx.x;
+            *reinterpret_cast<i32x4*>(def) = i32x4{task, e, row0, rows_word};
+            def[4] = slot;
+            defer_now = 1;
+            break;
+          }
           __builtin_amdgcn_s_sleep(8);
         }
+        s_task[7] = defer_now;
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
+      if (__builtin_amdgcn_readfirstlane(s_task[7])) {
+        have_def = true;
+        continue;
+      }
     }
     if (tracing && tid == 0 && (unsigned)slot < (unsigned)p.max_slots) {
       // the record's head now, its tail after the epilogue: no reading is kept through the
@@ -617,7 +707,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
             pend_slot[i] = (unsigned)slot < (unsigned)p.max_slots ? slot : 0;
           }
       }
-      if (++npend >= batch) release();
+      if (++npend >= batch || have_def) release();
     }
     __syncthreads();
   }

@@ -67,6 +67,11 @@ constexpr int kTaskMblkShift = 12;
 constexpr int kTaskMblkBits = 19;
 constexpr int kTaskNtMask = 0xFFF;
 constexpr int kDefaultSpinLimit = 1 << 22;
+// A Linear-2 tile whose m-block is still not ready after kDeferTicks of the 100 MHz real-time
+// counter (1 ms; a healthy wait lasts at most about one Linear-1 tile) is set aside in the
+// workgroup's deferral slot, and the workgroup runs tiles that cannot wait until it is ready.
+constexpr long long kDeferTicks = 100000;
+constexpr int kDeferSlots = 2048;  // workgroups with a deferral slot (others never defer)
 constexpr int kReleaseBatch = 2;  // Linear-1 completions a GEMM workgroup releases together
 // "no more tiles": all ones. Never a real task because m-block 0x7FFFF is out of range
 // (the host rejects plans with 2^19 - 1 or more m-blocks).
@@ -141,6 +146,8 @@ struct GemmArgs {
   int max_slots;            // capacity of the group record lists
   int spin_limit;
   int force_timeout;
+  int absent_group;      // MOE_FLAG_TEST_ABSENT_GROUP: this group's workgroups take no tile (-1: none)
+  int32_t* defer;        // [kDeferSlots][8]: each workgroup's deferred Linear-2 tile
   moe_trace_rec* trace;  // per-tile records (moe_config.trace), or null
 };
 

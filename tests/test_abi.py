@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 9
     for n in names:
         assert hasattr(lib, n), n
-    assert moe.abi_version() == 7
+    assert moe.abi_version() == 8
 
 
 
@@ -109,7 +109,7 @@ def test_auto_tile_height(T, k, E, tile):
     (dict(experts_per_wave=0), moe.MOE_ERR_INVALID_ARG),
     (dict(lead_waves=-1), moe.MOE_ERR_INVALID_ARG),
     (dict(tile_m=48), moe.MOE_ERR_UNSUPPORTED),
-    (dict(flags=16), moe.MOE_ERR_INVALID_ARG),
+    (dict(flags=32), moe.MOE_ERR_INVALID_ARG),
     (dict(flags=6), moe.MOE_ERR_INVALID_ARG),  # wide last m-blocks forced both on and off
     (dict(reserved=1), moe.MOE_ERR_INVALID_ARG),
     (dict(schedule=3), moe.MOE_ERR_INVALID_ARG),
