@@ -223,7 +223,7 @@ def main() -> int:
     ap.add_argument("--num-workgroups", type=int, default=0)
     ap.add_argument("--wide-tails", choices=["auto", "on", "off"], default="auto",
                     help="wide last m-blocks: the library's choice, forced on, or off (comparison)")
-    ap.add_argument("--trials", type=int, default=10,
+    ap.add_argument("--trials", type=int, default=20,
                     help="alternating trials per schedule (0 or --no-compare: the headline schedule only)")
     ap.add_argument("--no-compare", action="store_true", help="skip timing the other schedule")
     ap.add_argument("--others", default="tiny,dsv3_share,qwen3_30b_a3b,small_m_zipf",

@@ -106,7 +106,11 @@ __global__ __launch_bounds__(kAThreads, kAPerCU) void attn_fwd_kernel(AttnArgs a
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int i = 0; i < 16; ++i) oacc[c][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;  // the first block always raises the maximum
+    // running maximum (log2 units) and sum; the first block always raises the maximum (its
+    // eager sum against -1e30 is infinite). A finite start keeps every value NaN-free (masked
+    // keys are -inf, and -inf - (-1e30) is -inf), which lets this file be compiled without
+    // NaN semantics (-fno-honor-nans): the maxima then need no canonicalising instructions.
+    float m_run = -1.0e30f, l_run = 0.f;
 
     auto issue_k = [&](int t, int st) {
 #pragma unroll
@@ -218,8 +222,8 @@ __global__ __launch_bounds__(kAThreads, kAPerCU) void attn_fwd_kernel(AttnArgs a
         return fmaxf(mt, __shfl_xor(mt, 32)) * a.scale_log2;
       };
       // settles the block after its eager probabilities: raises the maximum if it must, or if
-      // the eager sum is not finite (the first block, against a maximum of -inf); testing
-      // the sum also keeps the eager exponentials ahead of the branch
+      // the eager sum is not finite (the first block, against the starting maximum of -1e30);
+      // testing the sum also keeps the eager exponentials ahead of the branch
       auto settle = [&](const f32x16& acc, bf16x8 (&pf)[2], float mt, float lsum) {
         if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy || !(lsum <= 3.0e38f))) {
           const float m_new = fmaxf(m_run, mt);
