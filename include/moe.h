@@ -14,7 +14,9 @@
  * The four calls follow the stages: moe_plan (route + expert histogram + prefix scan +
  * stable scatter + tile schedule), moe_dispatch (gather rows), moe_forward (persistent grouped
  * GEMM: Linear-1 with fused SwiGLU, then Linear-2), moe_combine (router-weighted sum).
- * moe_forward_gather is moe_dispatch + moe_forward in one launch (rows gathered on load).
+ * moe_forward_gather is moe_dispatch + moe_forward in one launch (rows gathered on load);
+ * moe_layer runs the whole layer as one launch, and moe_layer_noalloc the layer without a
+ * caller workspace. The attention forward of the same paper's second workload is in attn.h.
  *
  * Conventions for every call:
  *   - bfloat16 tensors are passed as uint16_t bit patterns; all tensors are dense row-major.
@@ -342,11 +344,11 @@ moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint1
  * rt, act, yd and out are byte-identical to them.
  *   logits, rt, x, w1, w2, act, yd, out, ws: as for those calls.
  * The workspace's phase counters (moe_ws_layout.layer_sync) must be zero before its first
- * moe_layer (a zero-filled workspace); every launch leaves them zero. The grid's workgroups wait for one another, so
- * they must all be resident at once: the grid is sized to the resident capacity, and a kernel
- * running concurrently on another stream can keep some from starting; every wait is bounded
- * (spin_limit), and an expired one records MOE_ERR_TIMEOUT (moe_status_read) with the outputs
- * undefined, and never hangs or faults. After moe_layer the workspace holds its plan, ready
+ * moe_layer (a zero-filled workspace); every launch leaves them zero. The grid's workgroups
+ * wait for one another at the phase barriers, so they must all be resident at once: the grid
+ * is sized to the resident capacity, and a kernel running concurrently on another stream can
+ * keep some from starting; every wait is bounded (spin_limit), and an expired one records
+ * MOE_ERR_TIMEOUT (moe_status_read) with the outputs undefined, and never hangs or faults. After moe_layer the workspace holds its plan, ready
  * for moe_forward / moe_forward_gather as after moe_plan. It always runs regular tiles (no
  * wide last m-blocks, whatever the flags say; the bytes are the same), so a later
  * moe_forward on that plan must be given MOE_FLAG_NO_WIDE_TAILS.
