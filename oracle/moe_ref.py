@@ -171,21 +171,3 @@ def moe_layer(x_bits, logits, w1, w2, k: int) -> dict:
     out = combine(yd, w, pos, T, k)
     return dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, pos=pos,
                 xd=xd, a=a, yd=yd, out=out)
-
-
-def token_rows(t: int, x_bits, ids, w, w1, w2):
-    """The layer for one token alone (rows of a GEMM are independent, so this is the same
-    definition restricted to one token). Returns (A bits [k, I], Yd bits [k, H], out bits [H])
-    with slot j's rows in position j."""
-    k = ids.shape[1]
-    a_rows, y_rows = [], []
-    for j in range(k):
-        a, y = expert_ffn(np.asarray(x_bits)[t:t + 1], w1[int(ids[t, j])], w2[int(ids[t, j])])
-        a_rows.append(a[0])
-        y_rows.append(y[0])
-    a_rows, y_rows = np.stack(a_rows), np.stack(y_rows)
-    acc = np.zeros(y_rows.shape[1], np.float64)
-    yf = bf16_to_f64(y_rows)
-    for j in range(k):
-        acc += float(np.float64(w[t, j])) * yf[j]
-    return a_rows, y_rows, f64_to_bf16_bits(bf16_round(acc))

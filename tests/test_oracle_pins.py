@@ -219,15 +219,3 @@ def test_exact_integer_case(k):
     np.testing.assert_array_equal(o["yd"][o["pos"]].reshape(T, k, -1), ex["y_tok"])
     np.testing.assert_array_equal(o["out"], ex["out"])
     assert np.all(o["counts"] > 0)
-
-
-def test_token_rows_equal_layer_rows():
-    s = W.shape(T=30, H=64, I=32, E=5, k=2, seed=14, x_std=1.0, w_std=0.1)
-    d = W.generate(s)
-    o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], s.k)
-    for t in (0, 7, 29):
-        a, y, out = R.token_rows(t, d["x"], o["ids"], o["w"], d["w1"], d["w2"])
-        rows = o["pos"][t * s.k:(t + 1) * s.k]
-        np.testing.assert_array_equal(a, o["a"][rows])
-        np.testing.assert_array_equal(y, o["yd"][rows])
-        np.testing.assert_array_equal(out, o["out"][t])
