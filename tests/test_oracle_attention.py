@@ -122,7 +122,9 @@ def _mutant(kind):
         q, k, v = bf16_to_f64(q_bits), bf16_to_f64(k_bits), bf16_to_f64(v_bits)
         d = q.shape[-1]
         s = np.matmul(q, np.swapaxes(k, -1, -2))
-        if kind != "no_scale":
+        if kind == "scale_by_d":
+            s = s / d
+        elif kind != "no_scale":
             s = s / np.sqrt(d)
         ax = -2 if kind == "softmax_over_queries" else -1
         e = np.exp(s - s.max(axis=ax, keepdims=True))
@@ -132,7 +134,7 @@ def _mutant(kind):
     return f
 
 
-@pytest.mark.parametrize("kind", ["no_scale", "softmax_over_queries", "swapped_operands"])
+@pytest.mark.parametrize("kind", ["no_scale", "scale_by_d", "softmax_over_queries", "swapped_operands"])
 def test_planted_mistakes_are_caught(kind):
     q, k, v = rand_qkv(1, 2, 40, 32, 30)
     bad = _mutant(kind)(q, k, v)
