@@ -76,6 +76,15 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
 __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voffset, uint32_t soffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, soffset, 0, 0);
 }
+// The same load as an instruction the compiler does not track: it then inserts no wait for it
+// (with the builtin it waits for every such load before each barrier), so loads may stay in
+// flight across barriers. The code that issues them waits for them itself (s_waitcnt vmcnt(n):
+// loads complete in issue order, so n leaves the n most recent in flight).
+__device__ inline void load_lds16_untracked(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voffset,
+                                            uint32_t soffset) {
+  const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
+}
 
 // silu(g) = g / (1 + e^-g), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
 // IEEE division: the result is rounded to bf16 right after, and 1 + e^-g is exactly 1 for
@@ -108,11 +117,18 @@ struct Interleave {
   }
 };
 
-// LDS bytes of a tile shape's two stages (weight rows then token rows, 64 K-columns each).
+// LDS of a tile shape: two stages of weight rows then token rows (64 K-columns each), and, where
+// the two stages already take more than half of a CU's LDS (so one workgroup runs per CU
+// anyway) and a third set of weight rows still fits, that third weight stage, so that the
+// weight rows can be loaded two K steps ahead of their use (W3).
+constexpr int kLdsBytes = 160 * 1024;  // LDS per CU
 template <int BM, int WN, int WM, bool WIDE>
 struct GemmLds {
   static constexpr bool WIDE_OK = WIDE && BM == 256 && WN == 2 && WM == 4;
-  static constexpr int BYTES = 2 * (WIDE_OK ? 2 * kTileN2 + BM / 2 : kTileN2 + BM) * kTileK * 2;
+  static constexpr int STAGE_BYTES = (WIDE_OK ? 2 * kTileN2 + BM / 2 : kTileN2 + BM) * kTileK * 2;
+  static constexpr int WSTAGE_BYTES = kTileN2 * kTileK * 2;
+  static constexpr bool W3 = !WIDE_OK && 2 * STAGE_BYTES > kLdsBytes / 2 && 2 * STAGE_BYTES + WSTAGE_BYTES <= kLdsBytes;
+  static constexpr int BYTES = 2 * STAGE_BYTES + (W3 ? WSTAGE_BYTES : 0);
 };
 
 // The planner's phases of the single-launch layer, on every workgroup of the grid: route the
@@ -216,19 +232,24 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
   static_assert(BM % RG == 0 && BN % (2 * RG) == 0 && RG % 16 == 0, "staging groups");
   static_assert(BN % 32 == 0 && BM % 32 == 0, "tile shape");
   static_assert(!WIDE_OK || (LD == LDN + BM / RG + 2 && (BM / 2) % RG == 0), "wide staging");
+  // W3: weight rows three-buffered. The LDS then holds [W0 T0 W1 T1 W2] (W: BN weight rows, T: BM
+  // token rows); token rows keep two stages, K step kt's weight rows sit in W(kt mod 3).
+  constexpr bool W3 = GemmLds<BM, WN, WM, WIDE>::W3;
+  constexpr int LDS_ELEMS = GemmLds<BM, WN, WM, WIDE>::BYTES / 2;
+  static_assert(GemmLds<BM, WN, WM, WIDE>::STAGE_BYTES == 2 * STAGE && (!W3 || LDN + BM / RG == LD), "LDS layout");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
   // The tile record, its record slot, the resume and defer flags and the exit flag live at the
-  // start of LDS stage 1: that stage is first written only after a barrier that every wave
-  // passes after reading them.
-  int* const s_task = reinterpret_cast<int*>(&lds[STAGE]);
+  // start of the first LDS stage the mainloop writes after its prologue barrier (stage 1, or
+  // W2): every wave passes that barrier after reading them.
+  int* const s_task = reinterpret_cast<int*>(&lds[W3 ? 2 * STAGE : STAGE]);
   int* const s_last = s_task + 5;
   // per-tile trace: only the TRACE instances (launched when a trace buffer is given) hold
   // any of its code, so the others are unchanged by it
   constexpr bool tracing = TRACE;
   // the single-launch layer plans first; the tile loop reads the header the plan writes
   bool plan_ok = true;
-  if constexpr (FUSED) plan_ok = layer_plan_phases<64 * WN * WM>(ka, lds, 2 * STAGE);
+  if constexpr (FUSED) plan_ok = layer_plan_phases<64 * WN * WM>(ka, lds, LDS_ELEMS);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = tid >> 3, lchunk = tid & 7;  // staging: row within an RG-row group, LDS chunk slot
@@ -541,13 +562,15 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     }
 
     // Mainloop, software-pipelined by hand. Per K step of 64 (four MFMA k-steps of 16):
-    //   the next K step's operands go straight into the other LDS stage (buffer->LDS loads)
+    //   the next K step's operands go straight into the other LDS stage (buffer->LDS loads);
+    //   with W3, the next K step's token rows and the weight rows of the one after it
     //   k-step 0 MFMAs | fragments of k-step 1
     //   k-step 1 MFMAs | fragments of k-step 2
     //   k-step 2 MFMAs | fragments of k-step 3
     //   k-step 3 MFMAs
-    //   wait for this wave's loads, barrier (the other stage is complete, this one free), then
-    //   fragments of the next K step's k-step 0
+    //   wait for this wave's loads (with W3, all but the weight rows two steps ahead), barrier
+    //   (the next K step's operands are complete, this step's stages free), then fragments of
+    //   the next K step's k-step 0
     // Fragments alternate between two register sets so that reads for k-step s + 1 are in
     // flight while the MFMAs of k-step s run; the sched_group_barrier patterns keep the
     // compiler from sinking the reads next to their first use.
@@ -576,14 +599,32 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
         }
       }
     };
-    auto read_frags = [&](int st, int ks, int set) {
-      const uint16_t* base = &lds[st * STAGE];
+    // W3 (regular tiles only): K step kt's token rows into stage st, or its weight rows into
+    // weight stage ws, with the untracked loads
+    auto issue_tokens = [&](int kt, int st) {
+      const uint32_t past = kt < KT ? 0u : 0x80000000u;
+      const uint32_t ks = (uint32_t)kt * BK * 2u;
+#pragma unroll
+      for (int i = LDN; i < LD; ++i)
+        load_lds16_untracked(r_t, &lds[st * STAGE + (wave_u * 8 + RG * i) * BK], vtok[i - LDN] | past, ks);
+    };
+    auto issue_weights = [&](int kt, int ws) {
+      const uint32_t vw = vbase_w | (kt < KT ? 0u : 0x80000000u);
+      const uint32_t ks = (uint32_t)kt * BK * 2u;
+#pragma unroll
+      for (int i = 0; i < LDN; ++i)
+        load_lds16_untracked(r_w, &lds[ws * STAGE + (wave_u * 8 + RG * i) * BK], vw, chunk_soff(i) + ks);
+    };
+    // fragments of k-step ks: weight rows from stage ws, token rows from stage st
+    auto read_frags = [&](int st, int ws, int ks, int set) {
+      const uint16_t* wbase = &lds[ws * STAGE];
+      const uint16_t* tbase = &lds[st * STAGE];
       const int pc = ((2 * ks + fr_chunk) ^ swz(fr_row)) * 8;
 #pragma unroll
-      for (int f = 0; f < FN; ++f) fa[set][f] = *reinterpret_cast<const bf16x8*>(base + (wrow[f] + fr_row) * BK + pc);
+      for (int f = 0; f < FN; ++f) fa[set][f] = *reinterpret_cast<const bf16x8*>(wbase + (wrow[f] + fr_row) * BK + pc);
 #pragma unroll
       for (int m = 0; m < FM; ++m)
-        fb[set][m] = *reinterpret_cast<const bf16x8*>(base + (bn + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
+        fb[set][m] = *reinterpret_cast<const bf16x8*>(tbase + (bn + wm * (BM / WM) + m * 32 + fr_row) * BK + pc);
     };
     auto mfmas = [&](int set) {
 #pragma unroll
@@ -593,34 +634,58 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
           acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][f], fb[set][m], acc[f][m], 0, 0, 0);
     };
     // one K step on LDS stage st (a constant at each call site); K step kt + 1 lands in the
-    // other stage meanwhile
+    // other stage meanwhile. W3: the step's weight rows are in stage wr (kt mod 3, a scalar
+    // kept across steps), and K step kt + 2's weight rows go to the third one, which held
+    // K step kt - 1's; they are left in flight at the step's end (issued last, they are the
+    // LDN most recent loads of this wave)
+    int wr = 0;
     auto step = [&](int st, int kt) {
       __builtin_amdgcn_sched_barrier(0);
-      issue_loads(kt + 1, st ^ 1);
+      if constexpr (W3) {
+        issue_tokens(kt + 1, st ^ 1);
+        issue_weights(kt + 2, wr == 0 ? 2 : wr - 1);
+      } else {
+        issue_loads(kt + 1, st ^ 1);
+      }
+      const int ws = W3 ? wr : st;
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, 1, 1);
+      read_frags(st, ws, 1, 1);
       mfmas(0);
       Interleave<FN * FM, 0, FN + FM, 0>::emit();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, 2, 0);
+      read_frags(st, ws, 2, 0);
       mfmas(1);
       Interleave<FN * FM, 0, FN + FM, 0>::emit();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(st, 3, 1);
+      read_frags(st, ws, 3, 1);
       mfmas(0);
       Interleave<FN * FM, 0, FN + FM, 0>::emit();
       __builtin_amdgcn_sched_barrier(0);
       mfmas(1);
       __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      read_frags(st ^ 1, 0, 0);
+      if constexpr (W3) {
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDN) : "memory");
+        __syncthreads();
+        wr = wr == 2 ? 0 : wr + 1;
+        read_frags(st ^ 1, wr, 0, 0);
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        read_frags(st ^ 1, st ^ 1, 0, 0);
+      }
     };
 
-    issue_loads(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (W3) {
+      issue_weights(0, 0);
+      issue_tokens(0, 0);
+      issue_weights(1, 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LDN) : "memory");
+    } else {
+      issue_loads(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     __syncthreads();
-    read_frags(0, 0, 0);
+    read_frags(0, 0, 0, 0);
     // two K steps per trip, so the stage index is a constant and the body one basic block
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
@@ -628,6 +693,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
       step(1, kt + 1);
     }
     if (kt < KT) step(0, kt);
+    // W3: the last step's loads past the end (they write zeros) must land before the epilogue
+    // reuses the stages
+    if constexpr (W3) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the epilogue's next task reuses both stages
     if (tracing && tid == 0 && (unsigned)slot < (unsigned)p.max_slots) p.trace[slot].t_epilogue = rt_clock();
 
@@ -713,7 +781,7 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
   }
 
   if constexpr (FUSED) {
-    layer_finish_phases<NT>(ka, lds, 2 * STAGE, plan_ok);
+    layer_finish_phases<NT>(ka, lds, LDS_ELEMS, plan_ok);
   } else {
     // the last workgroup to leave resets the cursor and the ready counters, so the next
     // moe_forward on this plan starts clean without a separate launch
