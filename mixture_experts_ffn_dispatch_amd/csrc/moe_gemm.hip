@@ -47,8 +47,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr unsigned kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit data format (gfx9)
-// cache-policy operand of gfx950 buffer instructions: sc1 (device scope)
+// cache-policy operand of gfx950 buffer instructions: sc1 (device scope), nt (streaming:
+// the lines are not kept for reuse)
 constexpr int kCachePolicySC1 = 16;
+constexpr int kCachePolicyNT = 2;
 // Claim result that tells the workgroup to release the completions it holds and claim again:
 // given when its own group's list runs out, so the holds are not kept through the scan of the
 // other groups' cursors (one atomic each). Never a task: m-block 0x7FFFF is out of range.
@@ -72,18 +74,25 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane L's bytes land at lds_dst + 16 L
-// (lds_dst is the same for the whole wavefront); voffset and soffset address the buffer only
+// (lds_dst is the same for the whole wavefront); voffset and soffset address the buffer only.
+// POLICY: the cache policy (0, or kCachePolicyNT for bytes no other load reads).
+template <int POLICY = 0>
 __device__ inline void load_lds16(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voffset, uint32_t soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, soffset, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, voffset, soffset, 0,
+                                           POLICY);
 }
 // The same load as an instruction the compiler does not track: it then inserts no wait for it
 // (with the builtin it waits for every such load before each barrier), so loads may stay in
 // flight across barriers. The code that issues them waits for them itself (s_waitcnt vmcnt(n):
 // loads complete in issue order, so n leaves the n most recent in flight).
+template <bool NT = false>
 __device__ inline void load_lds16_untracked(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voffset,
                                             uint32_t soffset) {
   const uint32_t m = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_dst;
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
+  if constexpr (NT)
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
+  else
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voffset), "s"(r), "s"(soffset), "{m0}"(m) : "memory");
 }
 
 // silu(g) = g / (1 + e^-g), with the hardware reciprocal (v_rcp_f32, about 1 ulp) instead of an
@@ -234,8 +243,8 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
   static_assert(!WIDE_OK || (LD == LDN + BM / RG + 2 && (BM / 2) % RG == 0), "wide staging");
   // W3: weight rows three-buffered. The LDS then holds [W0 T0 W1 T1 W2] (W: BN weight rows, T: BM
   // token rows); token rows keep two stages, K step kt's weight rows sit in W(kt mod 3).
-  constexpr bool W3 = GemmLds<BM, WN, WM, WIDE>::W3;
-  constexpr int LDS_ELEMS = GemmLds<BM, WN, WM, WIDE>::BYTES / 2;
+  constexpr bool W3 = GemmLds<BM, WN, WM, WIDE>::W3 && !FUSED;
+  constexpr int LDS_ELEMS = W3 ? GemmLds<BM, WN, WM, WIDE>::BYTES / 2 : 2 * STAGE;
   static_assert(GemmLds<BM, WN, WM, WIDE>::STAGE_BYTES == 2 * STAGE && (!W3 || LDN + BM / RG == LD), "LDS layout");
 
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
@@ -443,7 +452,9 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     const int resumed = __builtin_amdgcn_readfirstlane(s_task[6]);
     if (resumed) have_def = false;
     const bool wide = WIDE_OK && (rows_word & kRowsWide) != 0;
-    const int nrows = rows_word & ~kRowsWide;
+    // the expert's only m-block: its weight rows are read by this tile alone
+    const bool w_nt = (rows_word & kRowsOnce) != 0;
+    const int nrows = rows_word & ~kRowsFlags;
     // a plan this workspace could not have produced: skip the tile, report, never fault
     if (mb >= p.max_mblk || (unsigned)e >= (unsigned)p.E || row0 < 0 || nrows < 1 || row0 > p.R - nrows ||
         nt >= (l2 ? (p.H + kTileN2 - 1) / kTileN2 : p.n1) || (rows_word & kRowsWide && !WIDE_OK) ||
@@ -581,23 +592,35 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     // load. Past the last K step the offsets get bit 31 set, which is outside every buffer
     // range below 2^31 bytes: such loads fetch nothing. (A larger weight slab would read bytes
     // of its own buffer into a stage that is never used.)
+    // Weight chunks come first: 0 .. LDN - 1, and LDN .. 2 LDN - 1 of a wide tile; then the
+    // token chunks (LDN .. of a regular tile, 2 LDN .. of a wide one).
     auto issue_loads = [&](int kt, int st) {
       const uint32_t past = kt < KT ? 0u : 0x80000000u;
       const uint32_t vw = vbase_w | past;
+      const uint32_t ks = (uint32_t)kt * BK * 2u;
+      auto dst = [&](int i) -> uint16_t* { return &lds[st * STAGE + (wave_u * 8 + RG * i) * BK]; };
+      auto weights = [&](auto policy) {
+        constexpr int P = decltype(policy)::value;
 #pragma unroll
-      for (int i = 0; i < LD; ++i) {
-        uint16_t* dst = &lds[st * STAGE + (wave_u * 8 + RG * i) * BK];
-        const uint32_t ks = (uint32_t)kt * BK * 2u;
-        if (i < LDN) {
-          load_lds16(r_w, dst, vw, chunk_soff(i) + ks);
-        } else if (!WIDE_OK || i < 2 * LDN) {
-          // token chunk i - LDN of a regular tile, or weight chunk i of a wide one
-          const bool wch = WIDE_OK && wide;
-          load_lds16(wch ? r_w : r_t, dst, wch ? vw : (vtok[i - LDN] | past), (wch ? chunk_soff(i) : 0u) + ks);
-        } else if (wide) {
-          load_lds16(r_t, dst, vtok[i - 2 * LDN] | past, ks);  // token chunks of a wide tile
+        for (int i = 0; i < LDN; ++i) load_lds16<P>(r_w, dst(i), vw, chunk_soff(i) + ks);
+        if constexpr (WIDE_OK) {
+          if (wide) {
+#pragma unroll
+            for (int i = LDN; i < 2 * LDN; ++i) load_lds16<P>(r_w, dst(i), vw, chunk_soff(i) + ks);
+          }
+        }
+      };
+      if (w_nt) weights(std::integral_constant<int, kCachePolicyNT>{});
+      else weights(std::integral_constant<int, 0>{});
+      if constexpr (WIDE_OK) {
+        if (wide) {
+#pragma unroll
+          for (int i = 2 * LDN; i < LD; ++i) load_lds16(r_t, dst(i), vtok[i - 2 * LDN] | past, ks);
+          return;
         }
       }
+#pragma unroll
+      for (int i = LDN; i < LDN + BM / RG; ++i) load_lds16(r_t, dst(i), vtok[i - LDN] | past, ks);
     };
     // W3 (regular tiles only): K step kt's token rows into stage st, or its weight rows into
     // weight stage ws, with the untracked loads
@@ -611,9 +634,15 @@ __global__ __launch_bounds__(64 * WN * WM, MINW) void gemm_persistent_kernel(typ
     auto issue_weights = [&](int kt, int ws) {
       const uint32_t vw = vbase_w | (kt < KT ? 0u : 0x80000000u);
       const uint32_t ks = (uint32_t)kt * BK * 2u;
+      if (w_nt) {
 #pragma unroll
-      for (int i = 0; i < LDN; ++i)
-        load_lds16_untracked(r_w, &lds[ws * STAGE + (wave_u * 8 + RG * i) * BK], vw, chunk_soff(i) + ks);
+        for (int i = 0; i < LDN; ++i)
+          load_lds16_untracked<true>(r_w, &lds[ws * STAGE + (wave_u * 8 + RG * i) * BK], vw, chunk_soff(i) + ks);
+      } else {
+#pragma unroll
+        for (int i = 0; i < LDN; ++i)
+          load_lds16_untracked(r_w, &lds[ws * STAGE + (wave_u * 8 + RG * i) * BK], vw, chunk_soff(i) + ks);
+      }
     };
     // fragments of k-step ks: weight rows from stage ws, token rows from stage st
     auto read_frags = [&](int st, int ws, int ks, int set) {

@@ -84,6 +84,10 @@ constexpr int32_t kNopTask = 0x7FFFFFFE;
 // 256-row tiles, an m-block of at most 128 rows runs as tiles of 512 weight rows (two n-tiles,
 // the even one named in the task word) by 128 token rows; its odd n-tiles hold no-op records.
 constexpr int32_t kRowsWide = 1 << 30;
+// Bit of the same words that marks the only m-block of its expert: every weight byte the
+// m-block's tiles read is then read by no other tile, so those loads are non-temporal.
+constexpr int32_t kRowsOnce = 1 << 29;
+constexpr int32_t kRowsFlags = kRowsWide | kRowsOnce;
 
 // Task word: bit 31 = Linear-2, bits 30..12 = m-block, bits 11..0 = n-tile.
 __host__ __device__ inline int32_t make_task(int l2, int mblk, int nt) {

@@ -643,7 +643,7 @@ __device__ void scan_schedule_block(const PlanArgs& a, int* s_tmp, int* s_cnt, i
       a.mb_expert[mbase + i] = e;
       a.mb_row0[mbase + i] = ebase + i * BM;
       const int rows = min(BM, c - i * BM);
-      a.mb_rows[mbase + i] = rows | (a.wide_tails && 2 * rows <= BM ? kRowsWide : 0);
+      a.mb_rows[mbase + i] = rows | (a.wide_tails && 2 * rows <= BM ? kRowsWide : 0) | (nmb == 1 ? kRowsOnce : 0);
     }
     ebase += c;
     mbase += nmb;
@@ -761,7 +761,8 @@ __device__ void place_tile(const PlanArgs& a, const WaveTable& t, int nw, int ph
   rec[1] = e;
   rec[2] = off_e + ml * BM;
   rec[3] = min(BM, cnt_e - ml * BM);
-  if (a.wide_tails && 2 * rec[3] <= BM) {  // a wide m-block: even n-tiles cover two
+  if (nmb == 1) rec[3] |= kRowsOnce;
+  if (a.wide_tails && 2 * (rec[3] & ~kRowsFlags) <= BM) {  // a wide m-block: even n-tiles cover two
     rec[3] |= kRowsWide;
     if (nt & 1) rec = i32x4{kNopTask, -1, 0, 0};
   }

@@ -210,7 +210,7 @@ def test_task_list_matches_model(workload, long_workload, wave_workloads, which,
     for e in range(shape.E):
         first_mb.append(nxt)
         nxt += -(-int(counts[e]) // L["tile_m"])
-    NOP, WIDE = 0x7FFFFFFE, 1 << 30
+    NOP, WIDE, ONCE = 0x7FFFFFFE, 1 << 30, 1 << 29
     tm = L["tile_m"]
     mb_expert = [e for e in range(shape.E) for _ in range(-(-int(counts[e]) // tm))]
     n_wide = 0
@@ -231,7 +231,9 @@ def test_task_list_matches_model(workload, long_workload, wave_workloads, which,
             n_wide += wide
             assert tuple(decode(np.array([rec[0]]))[0]) == (ph, mb, nt)
             assert rec[1] == e and rec[2] == offsets[e] + i * tm
-            assert rec[3] == expect_rows | (WIDE if wide else 0)
+            # an expert's only m-block is marked: its weight rows are read by its tiles alone
+            once = -(-int(counts[e]) // tm) == 1
+            assert rec[3] == expect_rows | (WIDE if wide else 0) | (ONCE if once else 0)
     if tm == 256 and which == "long":
         assert n_wide > 0  # five of its experts end in a block of at most 128 rows
     # dependency safety: every Linear-2 tile comes after all Linear-1 tiles of its m-block
