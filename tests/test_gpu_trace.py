@@ -96,9 +96,12 @@ def test_trace_records_every_tile_in_order(name, schedule):
 
 
 def test_interleaved_order_runs_later_linear1_between_linear2_tiles():
-    # dsv3_share with lead 1: the Linear-1 tiles of wave i + 1 are claimed while wave i's
-    # Linear-2 tiles are still being claimed; in the Expert-Wave order every group claims all
-    # of wave i's Linear-2 tiles of its list before any Linear-1 tile of wave i + 1
+    # dsv3_share with lead 1: inside each locality group, the Linear-1 tiles of wave i + 1 are
+    # claimed while that group's Linear-2 tiles of wave i are being claimed; in the Expert-Wave
+    # order every group claims all of its wave-i Linear-2 tiles before any Linear-1 tile of
+    # wave i + 1. The windows are taken per group: a group's records are handed out by its own
+    # cursor, so its claims follow its list, while how far the groups drift apart (and so a
+    # window over all groups) depends on tile timing.
     s = W.shape("dsv3_share")
     dev = Device(W.generate(s))
     waves = s.waves
@@ -110,16 +113,24 @@ def test_interleaved_order_runs_later_linear1_between_linear2_tiles():
         r, ph, mb = check_trace(tr, recs, goff, hdr)
         table = b["ws"].cpu().numpy()[L["mblk_expert"]:L["mblk_expert"] + 4 * int(hdr[3])].view(np.int32)
         wave = table[mb] // s.experts_per_wave
-        res[schedule] = (r, ph, wave)
-    r, ph, wave = res[moe.MOE_SCHED_INTERLEAVED]
-    for i in range(waves - 1):
-        l2_last = r["t_claimed"][(ph == 1) & (wave == i)].max()
-        l2_first = r["t_claimed"][(ph == 1) & (wave == i)].min()
-        l1_next = r["t_claimed"][(ph == 0) & (wave == i + 1)]
-        inside = np.mean((l1_next > l2_first) & (l1_next < l2_last))
-        assert inside > 0.5, f"wave {i}: only {inside:.0%} of the next wave's Linear-1 tiles ran among its Linear-2 tiles"
-    r, ph, wave = res[moe.MOE_SCHED_EXPERT_WAVE]
-    for i in range(waves - 1):
-        l2_first = r["t_claimed"][(ph == 1) & (wave == i)].min()
-        l1_next = r["t_claimed"][(ph == 0) & (wave == i + 1)]
-        assert np.mean(l1_next > l2_first) > 0.95
+        slots = np.flatnonzero(recs[:, 0] != NOP)
+        group = np.searchsorted(goff, slots, side="right") - 1
+        inside = []
+        for i in range(waves - 1):
+            l2, l1 = (ph == 1) & (wave == i), (ph == 0) & (wave == i + 1)
+            n_in = n_all = 0
+            for g in range(8):
+                t2, t1 = r["t_claimed"][l2 & (group == g)], r["t_claimed"][l1 & (group == g)]
+                if len(t2) and len(t1):
+                    n_in += int(np.sum((t1 > t2.min()) & (t1 < t2.max())))
+                    n_all += len(t1)
+            inside.append(n_in / max(n_all, 1))
+        res[schedule] = inside
+        note(f"  schedule {schedule}: share of wave i+1 Linear-1 claims inside the group's wave-i "
+             f"Linear-2 claims: {[round(x, 2) for x in inside]}")
+    inter, ew = res[moe.MOE_SCHED_INTERLEAVED], res[moe.MOE_SCHED_EXPERT_WAVE]
+    # interleaved: every wave's next Linear-1 tiles are in part claimed among its Linear-2 tiles
+    # (how large a part depends on how the units fall to the groups: 0.35 to 0.82 here), half of
+    # them over all waves; Expert-Wave: none, but for claims racing at a unit boundary
+    assert min(inter) > 0.2 and np.mean(inter) > 0.5, inter
+    assert max(ew) < 0.05, ew
