@@ -108,6 +108,36 @@ def test_shape_sweep_full_parity(T, H, I, E, k, Wv, tile_m, schedule):
         assert torch.equal(b[key].view(torch.int16), bg[key].view(torch.int16)), key
 
 
+# Odd numbers of 64-wide K steps, down to one, on the instances that three-buffer their weight
+# rows (regular 256-row tiles, wide tails off, and 128-row tiles): the tail step after the
+# loop's pairs, a step whose next two K steps lie past the end, and a single K step.
+K_TAIL = [
+    # T, H, I, E, k, tile_m  (K steps: H / 64 for Linear-1, I / 64 for Linear-2)
+    (700, 64, 192, 3, 2, 256),    # 1 and 3
+    (520, 320, 64, 2, 1, 256),    # 5 and 1
+    (900, 192, 320, 4, 2, 256),   # 3 and 5, several m-blocks per expert
+    (300, 64, 320, 4, 2, 128),    # 1 and 5
+    (400, 448, 192, 6, 3, 128),   # 7 and 3
+    (200, 192, 64, 4, 1, 256),    # 3 and 1; every expert one m-block (non-temporal weight rows)
+    (120, 320, 192, 4, 2, 128),   # 5 and 3; every expert one m-block
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,k,tile_m", K_TAIL)
+def test_odd_k_steps_full_parity(T, H, I, E, k, tile_m):
+    s = W.shape(T=T, H=H, I=I, E=E, k=k, experts_per_wave=1, seed=T + H + I, x_std=1.0, w_std=0.05)
+    note(f"odd K steps {W.describe(s)} tile_m={tile_m}")
+    d = W.generate(s)
+    o = R.moe_layer(d["x"], d["logits"], d["w1"], d["w2"], k)
+    cfg = make_cfg(s, tile_m=tile_m, schedule=moe.MOE_SCHED_INTERLEAVED, flags=moe.MOE_FLAG_NO_WIDE_TAILS)
+    dev = Device(d)
+    b = run(cfg, dev)
+    check_full(fetch(b), o, host_bits(b["xd"]), E)
+    bg = run(cfg, dev, gather=True)
+    for key in ("act", "yd", "out"):
+        assert torch.equal(b[key].view(torch.int16), bg[key].view(torch.int16)), key
+
+
 def test_identical_experts_match_dense_ffn():
     s = W.shape(T=160, H=256, I=128, E=6, k=3, seed=21, x_std=1.0, w_std=0.05)
     note(f"identical experts {W.describe(s)}")
