@@ -868,12 +868,13 @@ hipError_t launch_variant(const GemmArgs& a, int num_workgroups, hipStream_t s) 
 template <int BM, int WN, int WM, int MINW, bool WIDE>
 hipError_t launch_layer_variant(const LayerArgs& a, int num_workgroups, hipStream_t s) {
   constexpr int NT = 64 * WN * WM;
-  // the planner's phases share the tile loop's LDS: the scan needs about 54 KiB
-  static_assert(GemmLds<BM, WN, WM, WIDE>::BYTES >= 32 * 4 + 4 * MOE_MAX_EXPERTS + 4 * (kWaveTableLds + 1) +
-                                                      8 * MOE_MAX_EXPERTS + 16,
+  // the planner's phases share the tile loop's LDS (the single-launch instances keep two
+  // stages): the scan needs about 54 KiB
+  constexpr int kFusedLds = 2 * GemmLds<BM, WN, WM, WIDE>::STAGE_BYTES;
+  static_assert(kFusedLds >= 32 * 4 + 4 * MOE_MAX_EXPERTS + 4 * (kWaveTableLds + 1) + 8 * MOE_MAX_EXPERTS + 16,
                 "LDS for the planner phases");
-  static_assert(GemmLds<BM, WN, WM, WIDE>::BYTES >= 4 * (NT / 64) * MOE_MAX_EXPERTS + 16 &&
-                GemmLds<BM, WN, WM, WIDE>::BYTES >= 4 * kWaveTableLds + 16, "LDS for the scatter");
+  static_assert(kFusedLds >= 4 * (NT / 64) * MOE_MAX_EXPERTS + 16 && kFusedLds >= 4 * kWaveTableLds + 16,
+                "LDS for the scatter");
   int grid = 0;
   hipError_t err = variant_grid<BM, WN, WM, MINW, WIDE>(num_workgroups, &grid);
   if (err != hipSuccess) return err;
