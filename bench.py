@@ -67,7 +67,7 @@ def kernel_source_sha() -> str:
     """Hash of the code (comments and blank lines left out) of the GEMM and of the planner that
     writes the tile order it walks: the profiled traffic belongs to exactly this code."""
     h = hashlib.sha256()
-    for f in ("moe_gemm.hip", "moe_internal.h", "moe_plan.hip"):
+    for f in ("moe_gemm.hip", "moe_internal.h", "moe_plan.hip", "moe_plan_dev.h"):
         with open(os.path.join(ROOT, "mixture_experts_ffn_dispatch_amd", "csrc", f), encoding="utf-8") as fh:
             for line in fh:
                 code = line.split("//", 1)[0].rstrip()
