@@ -18,14 +18,14 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Rows per GEMM tile for a routing-average of T*k/E rows per expert (the host does not know
 // the actual counts). The 256-row tile (eight wavefronts, two per SIMD) is the most efficient
-// per flop and wins from about 96 rows per expert on average despite its padding. Below that
+// per flop and wins from about 112 rows per expert on average despite its padding. Below that
 // the 128-row tile (one workgroup per CU, weight rows loaded two K steps ahead) streams the
 // weights best, and with skewed routing its fewer m-blocks per large expert re-read less; only
 // a few rows per expert (under 20) favour the 32-row tile, by a few percent. The 64-row tile
 // is still available explicitly (it wins, by ~2%, only for uniform routing near 48 rows).
 int auto_tile_m(const moe_config& c) {
   const double avg = (double)c.T * c.k / c.E;
-  if (avg >= 96) return 256;
+  if (avg >= 112) return 256;
   if (avg >= 20) return 128;
   return 32;
 }

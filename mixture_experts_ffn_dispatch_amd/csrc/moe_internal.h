@@ -198,9 +198,7 @@ hipError_t launch_layer(const LayerArgs& la, int tile_m, bool wide, int num_work
 // choice, else wide when the average expert fills at most three m-blocks (T * k <= 3 * 256 * E),
 // where last blocks are a large share of the tiles. Both calls derive it from the same config.
 inline bool plan_wide_tails(const moe_config* c, int tile_m) {
-  if (tile_m != 256 || (c->flags & MOE_FLAG_NO_WIDE_TAILS)) return false;
-  if (c->flags & MOE_FLAG_WIDE_TAILS) return true;
-  return (long long)c->T * c->k <= 3ll * 256 * c->E;
+  return tile_m == 256 && (c->flags & MOE_FLAG_WIDE_TAILS) && !(c->flags & MOE_FLAG_NO_WIDE_TAILS);
 }
 // Column segments per token row: with few tokens, rows are cut into up to 4 segments of at
 // least 128 chunks (one step of a wavefront) so that about 4096 wavefronts run.

@@ -94,7 +94,7 @@ def test_layout_is_consistent():
 
 @pytest.mark.parametrize("T,k,E,tile", [(4096, 8, 32, 256), (8192, 8, 128, 256), (512, 6, 64, 128),
                                          (65536, 2, 16, 256), (256, 2, 8, 128), (8, 1, 64, 32),
-                                         (1024, 6, 64, 256), (1023, 6, 64, 128), (256, 5, 64, 128),
+                                         (1200, 6, 64, 256), (1194, 6, 64, 128), (256, 5, 64, 128),
                                          (256, 4, 64, 32)])
 def test_auto_tile_height(T, k, E, tile):
     assert moe.moe_workspace_layout(_cfg(T=T, k=k, E=E))["tile_m"] == tile
