@@ -352,7 +352,7 @@ moe_status moe_combine(const moe_config* cfg, const moe_routing* rt, const uint1
  * MOE_ERR_TIMEOUT (moe_status_read) with the outputs undefined, and never hangs or faults. After moe_layer the workspace holds its plan, ready
  * for moe_forward / moe_forward_gather as after moe_plan. It always runs regular tiles (no
  * wide last m-blocks, whatever the flags say; the bytes are the same), so a later
- * moe_forward on that plan must be given MOE_FLAG_NO_WIDE_TAILS.
+ * moe_forward on that plan must not be given MOE_FLAG_WIDE_TAILS.
  * Errors: as moe_plan; MOE_ERR_INVALID_ARG for a non-NULL cfg->trace (trace the separate
  * calls); MOE_ERR_UNSUPPORTED with more than 64 expert waves when they also exceed the
  * workgroup's threads (512 for 256-row tiles, else 256). */

@@ -15,9 +15,9 @@
 //    the workgroup takes a Linear-2 tile or exits).
 //  * Linear-2 tile: waits (bounded) until all Linear-1 tiles of its m-block have released,
 //    then multiplies those A rows by 256 rows of W2[e] and stores Yd in bf16.
-//  * Wide last m-blocks (a second instance of the 256-row kernel): an m-block of at most 128
-//    rows runs as tiles of twice the weight rows by 128 token rows, so an expert's short last
-//    block needs half the tiles and puts no padding rows through the MFMAs.
+//  * Wide last m-blocks (a second instance of the 256-row kernel, when asked for): an m-block of
+//    at most 128 rows runs as tiles of twice the weight rows by 128 token rows, so an expert's
+//    short last block needs half the tiles and puts no padding rows through the MFMAs.
 //  * The MFMA A operand is the weight tile and the B operand the token tile, so one lane
 //    ends with four consecutive output columns of one token row; the epilogue stages them in
 //    LDS and stores whole row segments (16 bytes per lane).
